@@ -1,0 +1,144 @@
+"""fp64 CPU oracle for exact attention, forward and backward.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this module. The HIP library and its Python binding
+never import it, share no code with it, and never fall back to it.
+
+This is the *plain definition* the tiled method reaches exactly (up to rounding
+order): "FlashAttentionを1から" (ta-paperlens), section "最適化なのに、計算が増える",
+and "FlashAttention·FA4·FP4", section "첫 번째 비용", both state that the tiled
+algorithm is not an approximation and returns the same answer as standard attention.
+So the oracle materialises the full N x N score matrix S and probability matrix P,
+in float64, with numpy's matmul as the only library primitive.
+
+Definitions followed (the formula images on the pages were lost in extraction; the
+surrounding prose fixes them, and the readings are listed in the design notes):
+
+* scores  S = scale * Q K^T ("Triton 05: Flash Attention", section "코드 라인별 설명
+  (Forward)", inner-loop step 1; "FlashAttention·FA4·FP4", section "첫 번째 비용":
+  S = QK^T/sqrt(d)); the scale is applied before masking and the row max;
+* causal mask: key j is visible to query i iff j <= i ("Triton 05", section "Causal
+  Masking": future tokens are blocked by -inf);
+* safe softmax along each row: P_ij = exp(S_ij - m_i) / sum_k exp(S_ik - m_i),
+  m_i = max_k S_ik ("FlashAttentionを1から", section "タイリングを阻む、softmaxという壁");
+* output O = P V, and the saved row statistic LSE_i = m_i + ln sum_j exp(S_ij - m_i),
+  natural log ("Triton 05", section "LSE로 P 재계산 (Recomputation)");
+* backward, for an upstream gradient dO:
+    dV = P^T dO,  dP = dO V^T,
+    dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)      (the softmax Jacobian, written out),
+    dQ = scale * dS K,  dK = scale * dS^T Q.
+  ("Triton 05", sections "Softmax Gradient", "dKV 커널 수식", "dQ 커널 수식").
+  The oracle deliberately uses the Jacobian form sum_k P_ik dP_ik rather than the
+  shortcut D_i = rowsum(dO_i * O_i) the page introduces, so that the GPU's D vector
+  is checked against an independent computation; D is returned separately, computed
+  from its definition on the page, for that comparison.
+
+All arrays are per head: q (Nq, d), k (Nk, d), v (Nk, dv), do (Nq, dv).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _as_f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def scores(q, k, scale: float, causal: bool) -> np.ndarray:
+    """S = scale * Q K^T, with S_ij = -inf where the causal mask hides key j from query i."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    s = scale * (q @ k.T)
+    if causal:
+        nq, nk = s.shape
+        hidden = np.arange(nk)[None, :] > np.arange(nq)[:, None]
+        s[hidden] = -np.inf
+    return s
+
+
+def softmax_rows(s: np.ndarray):
+    """Safe softmax over each row. Returns (P, m, l) with m the row max, l = sum exp(s - m)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def forward(q, k, v, scale: float, causal: bool, return_p: bool = False):
+    """Exact attention forward for one head. Returns (O, LSE[, P]) in float64."""
+    s = scores(q, k, scale, causal)
+    p, m, l = softmax_rows(s)
+    o = p @ _as_f64(v)
+    lse = m + np.log(l)
+    if return_p:
+        return o, lse, p
+    return o, lse
+
+
+def forward_rows(q, k, v, scale: float, causal: bool, rows):
+    """Forward restricted to the query rows ``rows`` (same definition, fewer rows).
+
+    Row i of O and LSE depends only on q_i and all of K, V, so this is the plain
+    definition evaluated for a sample of rows -- used for spot checks at sizes
+    where materialising every row of S would be needlessly slow.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    q = _as_f64(q)
+    k = _as_f64(k)
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        hidden = np.arange(k.shape[0])[None, :] > rows[:, None]
+        s[hidden] = -np.inf
+    p, m, l = softmax_rows(s)
+    return p @ _as_f64(v), m + np.log(l)
+
+
+def backward(q, k, v, do, scale: float, causal: bool):
+    """Exact attention backward for one head.
+
+    Returns a dict with o, lse, dq, dk, dv and delta (D_i = rowsum(dO_i * O_i)),
+    all float64.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    o, lse, p = forward(q, k, v, scale, causal, return_p=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    delta = (do * o).sum(axis=1)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}
+
+
+def forward_bhnd(q, k, v, scale: float, causal: bool):
+    """Forward over a (B, H, N, d) batch, one head at a time. Returns O (B,H,N,d), LSE (B,H,N)."""
+    B, H, N, _ = q.shape
+    o = np.empty(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = forward(q[b, h], k[b, h], v[b, h], scale, causal)
+    return o, lse
+
+
+def backward_bhnd(q, k, v, do, scale: float, causal: bool):
+    """Backward over a (B, H, N, d) batch, one head at a time."""
+    B, H, N, d = q.shape
+    dv_dim = v.shape[3]
+    out = {
+        "o": np.empty((B, H, N, dv_dim)),
+        "lse": np.empty((B, H, N)),
+        "dq": np.empty((B, H, N, d)),
+        "dk": np.empty((B, H, N, d)),
+        "dv": np.empty((B, H, N, dv_dim)),
+        "delta": np.empty((B, H, N)),
+    }
+    for b in range(B):
+        for h in range(H):
+            r = backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+            for name, arr in r.items():
+                out[name][b, h] = arr
+    return out
