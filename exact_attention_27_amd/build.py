@@ -1,0 +1,66 @@
+"""Build libfa.so (the gfx950 attention kernels + C ABI) in-tree with hipcc.
+
+Usage: python -m exact_attention_27_amd.build [--verbose]
+
+Always recompiles. The library lands next to this file as ``libfa.so``; the compiler's
+per-kernel resource report (VGPR/AGPR/SGPR, LDS, spills, occupancy) is written to
+``kernel_resources.txt`` beside it.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfa.so")
+RESOURCES = os.path.join(HERE, "kernel_resources.txt")
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libfa.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Wall", "-Wno-unused-function",
+        # Keep the compiler from forming packed fp32 VALU instructions.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Rpass-analysis=kernel-resource-usage",
+        "-I", os.path.join(os.path.dirname(HERE), "include"),
+        "-o", LIB + ".tmp",
+    ] + [os.path.join(CSRC, s) for s in SOURCES]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    report = [ln for ln in proc.stderr.splitlines() if "remark:" in ln]
+    other = [ln for ln in proc.stderr.splitlines()
+             if "remark:" not in ln and "packed-fp32-ops" not in ln and ln.strip()]
+    if proc.returncode != 0:
+        sys.stderr.write("\n".join(other) + "\n")
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    os.replace(LIB + ".tmp", LIB)
+    with open(RESOURCES, "w") as f:
+        f.write("\n".join(_condense(report)) + "\n")
+    if verbose and other:
+        sys.stderr.write("\n".join(other) + "\n")
+    return LIB
+
+
+def _condense(lines):
+    out = []
+    for ln in lines:
+        msg = ln.split("remark:", 1)[1].strip()
+        out.append(msg.replace(" [-Rpass-analysis=kernel-resource-usage]", ""))
+    return out
+
+
+if __name__ == "__main__":
+    path = build(verbose="--verbose" in sys.argv)
+    print(path)

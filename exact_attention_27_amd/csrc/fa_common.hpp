@@ -1,0 +1,138 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// element types, the MFMA tiles, LDS fragment loads and fp32 -> 16-bit rounding.
+//
+// MFMA tile used everywhere: v_mfma_f32_32x32x16_{bf16,f16}, D(32x32,fp32) += A(32x16) B(16x32).
+// Lane layout (wave64, lane l, h = l/32, l32 = l%32), verified on gfx950:
+//   A operand : lane l holds A[m = l32][k = 8h + j], j = 0..7     (8 x 16-bit, one VGPR quad)
+//   B operand : lane l holds B[k = 8h + j][n = l32], j = 0..7
+//   D         : lane l, register i (0..15) holds D[m = 8(i/4) + 4h + (i%4)][n = l32]
+// So each lane owns one output column n and 16 rows of it. Register group t (i = 8t..8t+7)
+// of a D tile covers rows 16t + sigma_h(j), sigma_h(j) = 8(j/4) + 4h + (j%4); converted to
+// 16-bit, it is exactly the B operand of a k=16 step whose k index runs over those same
+// rows in the order sigma_h. Any A operand paired with it must use the same k order,
+// which the transposing LDS read below provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+// 8 packed 16-bit elements = one MFMA operand per lane.
+struct Frag {
+  u32x4 v;
+};
+
+struct BF16 {
+  typedef __bf16 elem;
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma(const Frag& a, const Frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                   __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+  }
+  // Two fp32 -> packed pair of bf16, round to nearest even.
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    __bf16 a = (__bf16)x, b = (__bf16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t bits) {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+  }
+};
+
+struct FP16 {
+  typedef _Float16 elem;
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma(const Frag& a, const Frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a.v),
+                                                  __builtin_bit_cast(f16x8, b.v), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    _Float16 a = (_Float16)x, b = (_Float16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Lane coordinates.
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---------------------------------------------------------------------------------------
+// Register group t (8 fp32 values, i = 8t..8t+7) of a D tile -> 16-bit operand fragment.
+template <typename T>
+__device__ __forceinline__ Frag pack_group(const f32x16& d, int t) {
+  Frag f;
+  f.v[0] = T::pack2(d[8 * t + 0], d[8 * t + 1]);
+  f.v[1] = T::pack2(d[8 * t + 2], d[8 * t + 3]);
+  f.v[2] = T::pack2(d[8 * t + 4], d[8 * t + 5]);
+  f.v[3] = T::pack2(d[8 * t + 6], d[8 * t + 7]);
+  return f;
+}
+
+// ---------------------------------------------------------------------------------------
+// LDS tiles hold 16-bit elements row-major with a row stride of `stride` elements.
+
+// Operand with k contiguous in memory: lane gets Mem[row0 + l32][k0 + 8h .. k0 + 8h + 7].
+// Serves as an A operand (rows = m) or a B operand (rows = n). One 16-byte LDS read.
+__device__ __forceinline__ Frag lds_frag_rows(const uint16_t* base, int stride, int row0, int k0) {
+  const int l = lane_id();
+  const uint16_t* p = base + (row0 + (l & 31)) * stride + k0 + ((l >> 5) << 3);
+  Frag f;
+  f.v = *reinterpret_cast<const u32x4*>(p);
+  return f;
+}
+
+// Operand whose k index runs down the rows of a row-major tile (the transpose of the tile):
+// lane gets Mem[krow0 + sigma_h(j)][m0 + l32] for j = 0..7, i.e. A[m][k] = Mem[k][m] with
+// k in the sigma order that matches pack_group(). Two ds_read_b64_tr_b16: within each group
+// of 16 lanes, source lane s addresses row (s/4) of a 4-row block at column 4(s%4); lane r of
+// the group receives column r of those 4 rows.
+__device__ __forceinline__ Frag lds_frag_cols(const uint16_t* base, int stride, int krow0, int m0) {
+  const int l = lane_id();
+  const int h = l >> 5;
+  const int col = m0 + (((l >> 4) & 1) << 4) + ((l & 3) << 2);
+  const int rsub = (l & 15) >> 2;
+  const uint16_t* p0 = base + (krow0 + 4 * h + rsub) * stride + col;
+  const uint16_t* p1 = p0 + 8 * stride;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p1));
+  Frag f;
+  u32x2 ua = __builtin_bit_cast(u32x2, a);
+  u32x2 ub = __builtin_bit_cast(u32x2, b);
+  f.v[0] = ua[0];
+  f.v[1] = ua[1];
+  f.v[2] = ub[0];
+  f.v[3] = ub[1];
+  return f;
+}
+
+// Global 16-byte load of 8 elements (zero when !valid).
+__device__ __forceinline__ u32x4 gload16(const uint16_t* p, bool valid) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return valid ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+__device__ __forceinline__ float wave_xor32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float wave_xor32_sum(float x) {
+  return x + __shfl_xor(x, 32, 64);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace fa

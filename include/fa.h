@@ -1,0 +1,124 @@
+/*
+ * fa.h -- C ABI of the exact IO-aware tiled attention library (libfa.so), gfx950.
+ *
+ * The library computes exact softmax attention, forward and backward, without
+ * materialising the N x N score or probability matrices:
+ *
+ *   forward   O = softmax(scale * Q K^T  [causal mask]) V,  plus the row log-sum-exp
+ *             LSE_i = m_i + ln(sum_j exp(S_ij - m_i)) (natural log), and nothing else.
+ *             Defined on "Triton 05: Flash Attention" (wonbeomjang.kr), sections
+ *             "Online Softmax", "코드 라인별 설명 (Forward)" and "LSE로 P 재계산";
+ *             the result is the standard attention result, not an approximation
+ *             ("FlashAttentionを1から", section "オンラインsoftmax").
+ *   backward  dQ, dK, dV for an upstream gradient dO, recomputing P = exp(S - LSE)
+ *             from the saved LSE and using D_i = rowsum(dO_i * O_i), in three kernels
+ *             (preprocess D; dK/dV with a pinned K/V tile; dQ with a pinned Q tile)
+ *             so that every output tile has exactly one writer and no atomics are used
+ *             ("Triton 05: Flash Attention", sections "Softmax Gradient" and
+ *             "3단계 커널 구조").
+ *
+ * Conventions shared by every entry point:
+ *
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV are contiguous row-major (B, H, N, d)
+ *              tensors of the element type `dtype`; LSE and delta are contiguous
+ *              (B, H, N) float32. No strides.
+ *   Types      dtype FA_FP16 (IEEE binary16) or FA_BF16 (bfloat16). Arithmetic is
+ *              fp32 inside (fp32 accumulation on the matrix cores); every fp32 ->
+ *              16-bit conversion rounds to nearest even.
+ *   Shapes     B, H, N >= 1; head dim d in {64, 128}. Any N is accepted (tails are
+ *              masked). Other head dims return FA_ERR_UNSUPPORTED -- never a slower
+ *              or approximate fallback.
+ *   Mask       causal = 0 (none) or 1: key j is visible to query i iff j <= i
+ *              ("Triton 05", section "Causal Masking"; Nq = Nk so top-left and
+ *              bottom-right alignment coincide).
+ *   Scale      finite and > 0 (1/sqrt(d) for standard attention).
+ *   Memory     all pointers are DEVICE pointers owned by the caller, 16-byte aligned.
+ *              The library never allocates, frees or retains memory and keeps no
+ *              global mutable state: calls are re-entrant. Outputs must not overlap
+ *              inputs or each other.
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work is
+ *              enqueued on it and the call returns without synchronising; buffers
+ *              must stay alive until the stream reaches that point.
+ *   Errors     arguments are validated on the host before anything is enqueued:
+ *              FA_ERR_INVALID_ARG for null/misaligned/overlapping pointers,
+ *              non-positive sizes, 64-bit size overflow, unknown dtype, a causal
+ *              flag other than 0/1, or a non-finite / non-positive scale;
+ *              FA_ERR_UNSUPPORTED for a valid request this build does not implement
+ *              (head dim other than 64/128); FA_ERR_HIP if a kernel launch reports an
+ *              error. Faults during execution surface at the caller's next
+ *              synchronisation, as usual for HIP.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_HIP = 3
+} fa_status;
+
+/*
+ * Forward pass.
+ *   q, k, v  in : (B, H, N, d) dtype.
+ *   o        out: (B, H, N, d) dtype, fully overwritten.
+ *   lse      out: (B, H, N) float32, natural-log row log-sum-exp of the scaled,
+ *                 masked scores; fully overwritten. May be NULL when no backward
+ *                 pass will follow (inference); then it is not written.
+ * One kernel launch. Returns an fa_status.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, int dtype,
+               void* stream);
+
+/*
+ * Backward pass.
+ *   q, k, v  in : the forward inputs.
+ *   o, lse   in : the forward outputs for the same (scale, causal).
+ *   dO       in : (B, H, N, d) dtype, gradient of the loss w.r.t. O.
+ *   dq,dk,dv out: (B, H, N, d) dtype, fully overwritten (no zero-fill needed).
+ *   delta    out: (B, H, N) float32 caller-provided workspace; on return (in stream
+ *                 order) it holds D_i = sum_c dO_ic * O_ic, computed from the stored
+ *                 O. Must not be NULL.
+ * Three kernel launches on `stream`, in order: preprocess (delta), dK/dV, dQ.
+ * Returns an fa_status.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                float* delta, int B, int H, int N, int d, int causal, float scale,
+                int dtype, void* stream);
+
+/*
+ * The three backward stages, individually. fa_backward() is exactly these three calls in
+ * this order on one stream; they are exported so a caller can interleave its own work or
+ * time each kernel. Arguments have the same meaning, rules and errors as in fa_backward().
+ *   fa_backward_preprocess  delta_i = sum_c dO_ic * O_ic            ("Triton 05", "3단계 커널
+ *                           구조", stage 1). Reads o, dO; writes delta.
+ *   fa_backward_dkv         dK, dV with one K/V tile pinned per workgroup, looping over Q
+ *                           tiles (stage 2). Reads q, k, v, dO, lse, delta; writes dk, dv.
+ *   fa_backward_dq          dQ with one Q tile pinned per workgroup, looping over K/V tiles
+ *                           (stage 3). Reads q, k, v, dO, lse, delta; writes dq.
+ */
+int fa_backward_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
+                           int dtype, void* stream);
+int fa_backward_dkv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                    const float* delta, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                    float scale, int dtype, void* stream);
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                   const float* delta, void* dq, int B, int H, int N, int d, int causal, float scale,
+                   int dtype, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

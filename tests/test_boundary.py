@@ -1,0 +1,115 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects bad
+arguments with the documented status codes before any HIP call (no GPU is touched)."""
+import ctypes
+import math
+
+import pytest
+
+from tests import _lib
+
+import exact_attention_27_amd as fa
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.ensure_built()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _lib.header_functions()
+    assert set(declared) == set(fa.EXPORTED_SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in include/fa.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+        s = fa.fa_status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in fa.fa_status_string(99)
+
+
+# Fake device addresses: never dereferenced, because every call below fails validation
+# before anything is enqueued.
+A = [0x10000 * (i + 1) * 0x1000 for i in range(10)]
+
+
+def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0):
+    vp = ctypes.c_void_p
+    return lib.fa_forward(vp(q), vp(k), vp(v), vp(o), vp(lse), B, H, N, d, causal, scale, dtype, vp(0))
+
+
+def bwd(lib, ptrs=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0):
+    vp = ctypes.c_void_p
+    p = list(A) if ptrs is None else ptrs
+    return lib.fa_backward(*(vp(x) for x in p), B, H, N, d, causal, scale, dtype, vp(0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k=A[1] + 8), fa.FA_ERR_INVALID_ARG),          # misaligned
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=math.inf), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A[0]), fa.FA_ERR_INVALID_ARG),               # output aliases an input
+    (dict(lse=A[0] + 16), fa.FA_ERR_INVALID_ARG),        # lse inside q
+    (dict(B=1 << 20, H=1 << 20, N=1 << 20, d=64), fa.FA_ERR_INVALID_ARG),  # size overflow
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_forward_validation(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, N=0) == fa.FA_ERR_INVALID_ARG
+    assert bwd(lib, d=80) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lib, scale=math.nan) == fa.FA_ERR_INVALID_ARG
+    assert bwd(lib, causal=-1) == fa.FA_ERR_INVALID_ARG
+    assert bwd(lib, dtype=7) == fa.FA_ERR_INVALID_ARG
+    for i in range(10):  # every pointer is required (delta included)
+        p = list(A)
+        p[i] = 0
+        assert bwd(lib, ptrs=p) == fa.FA_ERR_INVALID_ARG
+    p = list(A)
+    p[6] = A[0]  # dq aliases q
+    assert bwd(lib, ptrs=p) == fa.FA_ERR_INVALID_ARG
+    p = list(A)
+    p[8] = A[7]  # dv aliases dk
+    assert bwd(lib, ptrs=p) == fa.FA_ERR_INVALID_ARG
+    p = list(A)
+    p[9] = A[2] + 32  # delta misaligned? no: 32 is aligned, but inside v
+    assert bwd(lib, ptrs=p) == fa.FA_ERR_INVALID_ARG
+
+
+def test_stage_validation(lib):
+    vp = ctypes.c_void_p
+    # preprocess: o, dO, delta
+    assert lib.fa_backward_preprocess(vp(0), vp(A[1]), vp(A[2]), 1, 1, 16, 64, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_preprocess(vp(A[0]), vp(A[1]), vp(A[0]), 1, 1, 16, 64, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_preprocess(vp(A[0]), vp(A[1]), vp(A[2]), 1, 1, 16, 48, 0, vp(0)) == fa.FA_ERR_UNSUPPORTED
+    # dkv: q k v dO lse delta dk dv
+    args = [vp(x) for x in A[:8]]
+    assert lib.fa_backward_dkv(*args[:6], vp(0), args[7], 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dkv(*args[:6], args[6], args[0], 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dkv(*args, 1, 1, 16, 64, 3, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    # dq: q k v dO lse delta dq
+    assert lib.fa_backward_dq(*args[:6], args[5], 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dq(*args[:6], vp(0), 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dq(*args[:7], 1, 1, 16, 64, 0, -0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 16, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fa_forward(q, q, q, q.clone(), None, False, 0.125)
