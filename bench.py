@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention path on one MI355X.
+
+One step = one full pass of the hot path over one batch of synthetic input resident in HBM:
+fa_forward (O, LSE) followed by the backward (preprocess delta, dK/dV, dQ -- the three
+stages fa_backward runs, launched individually here so each kernel can be timed with HIP
+events on the stream it runs on).
+
+Workload (default): B=4, H=32, N=4096, d=128, causal, bf16, Q, K, V, dO ~ N(0,1) from seed
+1004, scale = 1/sqrt(d). Counted FLOPs: forward F = 4*B*H*N^2*d, halved for causal
+("Triton 05: Flash Attention", section on why throughput stops at a fraction of peak: the
+two matmuls of the forward); backward 2.5 F; a step counts 3.5 F.
+
+Prints ONE JSON line on stdout. Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_common.hpp"],
+    "bwd_preprocess": ["fa_bwd.hip", "fa_common.hpp"],
+    "bwd_dkv": ["fa_bwd.hip", "fa_common.hpp"],
+    "bwd_dq": ["fa_bwd.hip", "fa_common.hpp"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_attention_27_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter runs, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = table.get(kernel)
+    if not rec or rec.get("workload") != workload or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(bits, w, heads):
+    """The fp64 oracle as it stands, on a bounded sample of heads of the same workload."""
+    import numpy as np
+    import fa_inputs as FI
+    from oracle import attention as ORACLE
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity count
+        threads = len(os.sched_getaffinity(0))
+    causal = w.causal[0]
+    t0 = time.perf_counter()
+    for b, h in heads:
+        q, k, v, do = (FI.bits_to_f64(bits[n][b, h], w.dtype) for n in FI.TENSOR_ORDER)
+        ORACLE.backward(q, k, v, do, w.scale(), causal)
+    dt = time.perf_counter() - t0
+    per_head = 3.5 * 4.0 * w.N * w.N * w.d * (0.5 if causal else 1.0)
+    return {
+        "value": len(heads) * per_head / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(heads)} of {w.B * w.H} heads (every {w.B * w.H // len(heads)}th (b, h)) of the "
+                   f"same workload: fp64 forward+backward materialising S and P, {dt:.2f} s wall; "
+                   f"counted 3.5*F per head as for the GPU"),
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llm_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run one plain device-to-device copy of this many MiB "
+                         "(a kernel of known traffic for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path shards over batch*heads with no communication, but no multi-GPU run is provided.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import fa_inputs as FI
+    import exact_attention_27_amd as fa
+
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU visible")
+        sys.exit(1)
+    fa.load_library()  # raises if libfa.so was not built: there is no fallback
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    w = FI.WORKLOADS[args.workload]
+    causal = w.causal[0]
+    scale = w.scale()
+    log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs; "
+        f"workload {w.label}")
+
+    t0 = time.perf_counter()
+    bits = FI.draw_workload(w)
+    torch_dt = torch.bfloat16 if w.dtype == FI.BF16 else torch.float16
+
+    def up(name):
+        return torch.from_numpy(bits[name].view(np.int16)).to(dev).view(torch_dt)
+
+    q, k, v, do = (up(n) for n in FI.TENSOR_ORDER)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    torch.cuda.synchronize()
+    log(f"inputs drawn and resident in HBM in {time.perf_counter() - t0:.1f} s")
+
+    stream = torch.cuda.current_stream(dev)
+    names = ["fwd", "bwd_preprocess", "bwd_dkv", "bwd_dq"]
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        fa.fa_forward(q, k, v, o, lse, causal, scale, stream)
+        if evs:
+            evs[1].record(stream)
+        fa.fa_backward_preprocess(o, do, delta, stream)
+        if evs:
+            evs[2].record(stream)
+        fa.fa_backward_dkv(q, k, v, do, lse, delta, dk, dv, causal, scale, stream)
+        if evs:
+            evs[3].record(stream)
+        fa.fa_backward_dq(q, k, v, do, lse, delta, dq, causal, scale, stream)
+        if evs:
+            evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step(ev[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    kern_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+               for i, n in enumerate(names)}
+    log("per-kernel mean ms: " + ", ".join(f"{n}={t:.4f}" for n, t in kern_ms.items()))
+
+    F = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if causal else 1.0)
+    step_flops = 3.5 * F
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = F / (kern_ms["fwd"] * 1e-3) / 1e12
+    bwd_ms = kern_ms["bwd_preprocess"] + kern_ms["bwd_dkv"] + kern_ms["bwd_dq"]
+    bwd_tflops = 2.5 * F / (bwd_ms * 1e-3) / 1e12
+
+    # Algorithmic work per launch: forward F; dK/dV kernel 2F (S, dP,
+    # dV, dK); dQ kernel 0.5F (dQ only -- its S and dP recomputation is the price of having
+    # no atomics and is not counted); preprocess reads O and dO and writes delta (bytes).
+    rows = w.B * w.H * w.N
+    algo = {
+        "fwd": ("mfma", F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_dkv": ("mfma", 2.0 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_dq": ("mfma", 0.5 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_preprocess": ("hbm", (2 * rows * w.d * 2 + rows * 4) / 1e9, "GB/s", PEAK_HBM_GBS),
+    }
+    dominant = max(kern_ms, key=kern_ms.get)
+    bound, work, unit, peak = algo[dominant]
+    achieved = work / (kern_ms[dominant] * 1e-3)
+    roofline = {
+        "bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+        "traffic": traffic_for(dominant, w.key), "kernel": dominant, "ms": kern_ms[dominant],
+    }
+    kernels = {}
+    for n in names:
+        b_, wk, u, pk = algo[n]
+        a_ = wk / (kern_ms[n] * 1e-3)
+        kernels[n] = {"ms": kern_ms[n], "achieved": a_, "unit": u, "frac": a_ / pk,
+                      "traffic": traffic_for(n, w.key)}
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = max(1, min(args.cpu_heads, w.B * w.H))
+        heads = [(i // w.H, i % w.H) for i in range(0, w.B * w.H, w.B * w.H // n)][:n]
+        log(f"timing the fp64 oracle on {len(heads)} head(s) on the host ...")
+        cpu = cpu_baseline(bits, w, heads)
+
+    line = {
+        "metric": "fwd+bwd attention TFLOP/s and % of bf16 MFMA peak, N=4096 d=128 causal",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == FI.BF16 else "fp16",
+        "data": "synthetic (seeded N(0,1), fixed before any result)",
+        "config": {"workload": w.label, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+                   "seed": w.seed, "counted_flop_per_step": step_flops},
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "fwd_tflops": fwd_tflops,
+        "fwd_frac_of_peak": fwd_tflops / PEAK_BF16_TFLOPS,
+        "bwd_tflops": bwd_tflops,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
