@@ -34,6 +34,10 @@ def build(verbose: bool = False) -> str:
         "-Wall", "-Wno-unused-function",
         # Keep the compiler from forming packed fp32 VALU instructions.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # Give MFMA results VGPR destinations: the kernels feed S and dP straight to VALU
+        # softmax code, and AGPR-destination MFMAs made the allocator shuttle accumulators
+        # between the two register files on every loop iteration.
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Rpass-analysis=kernel-resource-usage",
         "-I", os.path.join(os.path.dirname(HERE), "include"),
         "-o", LIB + ".tmp",

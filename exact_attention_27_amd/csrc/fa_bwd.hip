@@ -46,17 +46,15 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
 // ------------------------------------------------------------------------------------------
 // [2] dK, dV. Workgroup = NW waves, each owning 32 keys; Q/dO tiles of BQ rows stream
 // through a double-buffered LDS ring together with their LSE and D values.
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, float c_log2) {
   constexpr int BK = NW * 32;
-  constexpr int BQ = 64;
   constexpr int QBS = BQ / 32;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SQ = D + 32;           // stride of the Q and dO tiles (row and transposed reads)
   constexpr int NT = NW * 64;
   constexpr int CHUNKS = BQ * D / 8;
   static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly over the workgroup");
@@ -64,8 +62,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
   constexpr int CPR = D / 8;
   static_assert(NT >= 2 * BQ, "LSE and D staging needs 2*BQ threads");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BQ * SQ];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BQ * SQ];
+  // Q and dO tiles are read both by rows and transposed: swizzled layout.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float lds_lse[2][BQ];
   __shared__ __attribute__((aligned(16))) float lds_dl[2][BQ];
 
@@ -75,9 +74,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int kt = bid / BH;  // causal: low key tiles see the most queries and go first
+  // A head's K tiles run together on one XCD (shared Q/dO reads in its L2); causal: low
+  // key tiles see the most queries and go first.
+  const int n_ktiles = (N + BK - 1) / BK;
+  const int lid = xcd_local_index(blockIdx.x, BH * n_ktiles);
+  const int bh = lid / n_ktiles;
+  const int kt = lid % n_ktiles;
   const int k0 = kt * BK;
   const int kw0 = k0 + wave * 32;
 
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&lds_q[buf][row * SQ + col]) = pq[i];
-      *reinterpret_cast<u32x4*>(&lds_do[buf][row * SQ + col]) = pdo[i];
+      *reinterpret_cast<u32x4*>(&lds_q[buf][swz_off<D>(row, col)]) = pq[i];
+      *reinterpret_cast<u32x4*>(&lds_do[buf][swz_off<D>(row, col)]) = pdo[i];
     }
     if (tid < BQ) lds_lse[buf][tid] = pstat;
     else if (tid < 2 * BQ) lds_dl[buf][tid - BQ] = pstat;
@@ -152,10 +154,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
 
   for (int it = it_begin; it < it_end; ++it) {
     const int buf = (it - it_begin) & 1;
-    if (it + 1 < it_end) gload_tile(it + 1);
+    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle
+    // buffer): predicated loads would turn the staging registers into loop phis.
+    gload_tile(it + 1 < it_end ? it + 1 : it);
     const int qbase = it * BQ;
-    const bool skip = CAUSAL && (kw0 > qbase + BQ - 1);
-    if (!skip) {
+    // Every wave runs every Q tile of the workgroup's range: a tile entirely before this
+    // wave's keys is fully masked (P = 0), which keeps the loop body free of branches
+    // around the accumulators.
+    {
       const bool need_mask = (kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qbase);
       const uint16_t* qs = lds_q[buf];
       const uint16_t* dos = lds_do[buf];
@@ -171,8 +177,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = T::mfma(lds_frag_rows(qs, SQ, qb * 32, ks * 16), kf[ks], s);
-          dp = T::mfma(lds_frag_rows(dos, SQ, qb * 32, ks * 16), vf[ks], dp);
+          s = T::mfma(swz_frag_rows<D>(qs, qb * 32, ks * 16), kf[ks], s);
+          dp = T::mfma(swz_frag_rows<D>(dos, qb * 32, ks * 16), vf[ks], dp);
         }
         // rows of this lane: q_local = 32qb + 8g + 4h + r, i = 4g + r
 #pragma unroll
@@ -203,11 +209,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
         for (int qb = 0; qb < QBS; ++qb)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            acc_dv[db] = T::mfma(lds_frag_cols(dos, SQ, qb * 32 + tt * 16, db * 32), pf[qb][tt], acc_dv[db]);
-            acc_dk[db] = T::mfma(lds_frag_cols(qs, SQ, qb * 32 + tt * 16, db * 32), dsf[qb][tt], acc_dk[db]);
+            acc_dv[db] = T::mfma(swz_frag_cols<D>(dos, qb * 32 + tt * 16, db * 32), pf[qb][tt], acc_dv[db]);
+            acc_dk[db] = T::mfma(swz_frag_cols<D>(qs, qb * 32 + tt * 16, db * 32), dsf[qb][tt], acc_dk[db]);
           }
     }
-    if (it + 1 < it_end) lds_store_tile(buf ^ 1);
+    lds_store_tile(buf ^ 1);
     __syncthreads();
   }
 
@@ -242,16 +248,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int KB = BN / 32;
-  constexpr int SK = D + 16;   // K tile: row reads (S^T) and transposed reads (dQ)
-  constexpr int SV = D + 8;    // V tile: row reads only
   constexpr int NT = NW * 64;
   constexpr int CHUNKS = BN * D / 8;
   static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly over the workgroup");
   constexpr int CPT = CHUNKS / NT;
   constexpr int CPR = D / 8;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * SV];
+  // K is read by rows (S^T) and transposed (dQ), V by rows: swizzled layout for both.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -259,9 +264,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int qt = CAUSAL ? (n_qtiles - 1 - bid / BH) : (bid / BH);
+  // A head's Q tiles run together on one XCD (shared K/V reads in its L2), heaviest
+  // causal tile first.
+  const int lid = xcd_local_index(blockIdx.x, BH * n_qtiles);
+  const int bh = lid / n_qtiles;
+  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * QB * 32;
 
@@ -312,8 +319,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&lds_k[buf][row * SK + col]) = pk[i];
-      *reinterpret_cast<u32x4*>(&lds_v[buf][row * SV + col]) = pv[i];
+      *reinterpret_cast<u32x4*>(&lds_k[buf][swz_off<D>(row, col)]) = pk[i];
+      *reinterpret_cast<u32x4*>(&lds_v[buf][swz_off<D>(row, col)]) = pv[i];
     }
   };
 
@@ -323,10 +330,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) gload_tile(t + 1);
+    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle
+    // buffer): predicated loads would turn the staging registers into loop phis.
+    gload_tile(t + 1 < ntiles ? t + 1 : t);
     const int kbase = t * BN;
-    const bool skip = CAUSAL && (kbase > qw0 + QB * 32 - 1);
-    if (!skip) {
+    // Every wave runs every K/V tile of the workgroup's range (fully masked tiles add 0).
+    {
       const bool need_mask = (kbase + BN > N) || (CAUSAL && (kbase + BN - 1 > qw0));
       const uint16_t* ks_base = lds_k[buf];
       const uint16_t* vs_base = lds_v[buf];
@@ -344,8 +353,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const Frag ak = lds_frag_rows(ks_base, SK, kb * 32, ks * 16);
-          const Frag av = lds_frag_rows(vs_base, SV, kb * 32, ks * 16);
+          const Frag ak = swz_frag_rows<D>(ks_base, kb * 32, ks * 16);
+          const Frag av = swz_frag_rows<D>(vs_base, kb * 32, ks * 16);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             s[qb][kb] = T::mfma(ak, qf[qb][ks], s[qb][kb]);
@@ -377,12 +386,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const Frag a = lds_frag_cols(ks_base, SK, kb * 32 + tt * 16, db * 32);
+            const Frag a = swz_frag_cols<D>(ks_base, kb * 32 + tt * 16, db * 32);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb][db] = T::mfma(a, dsf[qb][kb][tt], acc[qb][db]);
           }
     }
-    if (t + 1 < ntiles) lds_store_tile(buf ^ 1);
+    lds_store_tile(buf ^ 1);
     __syncthreads();
   }
 
@@ -420,11 +429,11 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dkv_t(const BwdArgs& a) {
-  constexpr int NW = 4;
+  constexpr int NW = 4, BQ = 32;
   constexpr int BK = NW * 32;
   const int n_ktiles = (a.N + BK - 1) / BK;
   const long long grid = (long long)n_ktiles * a.BH;
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, BQ, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.BH, a.N, a.scale,
                      a.c_log2);
@@ -433,7 +442,7 @@ static hipError_t launch_dkv_t(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a) {
-  constexpr int NW = 4, QB = 1, BN = 64;
+  constexpr int NW = 4, QB = 1, BN = 32;
   constexpr int BM = NW * QB * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
   const long long grid = (long long)n_qtiles * a.BH;

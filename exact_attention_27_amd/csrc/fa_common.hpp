@@ -25,6 +25,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define FA_LDS __attribute__((address_space(3)))
 
@@ -40,10 +43,10 @@ struct BF16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
                                                    __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
   }
-  // Two fp32 -> packed pair of bf16, round to nearest even.
+  // Two fp32 -> packed pair of bf16, round to nearest even (one v_cvt_pk_bf16_f32).
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
-    __bf16 a = (__bf16)x, b = (__bf16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
   static __device__ __forceinline__ float to_f32(uint16_t bits) {
     return __builtin_bit_cast(float, (uint32_t)bits << 16);
@@ -58,8 +61,8 @@ struct FP16 {
                                                   __builtin_bit_cast(f16x8, b.v), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
-    _Float16 a = (_Float16)x, b = (_Float16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
   static __device__ __forceinline__ float to_f32(uint16_t bits) {
     return (float)__builtin_bit_cast(_Float16, bits);
@@ -117,6 +120,69 @@ __device__ __forceinline__ Frag lds_frag_cols(const uint16_t* base, int stride, 
   f.v[2] = ub[0];
   f.v[3] = ub[1];
   return f;
+}
+
+// ---------------------------------------------------------------------------------------
+// Swizzled tiles: rows of D 16-bit elements (D/8 chunks of 16 bytes), no padding, with
+// chunk c of row r stored at chunk c ^ swz(r). The row permutation makes both access
+// patterns the kernels use on the same tile free of LDS bank conflicts (64 banks x 4 B):
+//   row reads  - 16 lanes read one 16-byte chunk from 16 consecutive rows;
+//   transposing reads - 32 lanes read 8 bytes each from 4 consecutive rows x 4 chunks;
+// and keeps the 16-byte staging writes (one row per 16 lanes) conflict-free too.
+//   D = 128 (16 chunks): swz(r) = bits (r1 r0 r3 r2) of r, i.e. ((r & 3) << 2) | ((r >> 2) & 3)
+//   D = 64  (8 chunks, two rows per bank line): swz(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "swizzle defined for head dims 64 and 128");
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Element offset of (row, col) in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz<D>(row)) << 3) | (col & 7));
+}
+
+// lds_frag_rows() on a swizzled tile.
+template <int D>
+__device__ __forceinline__ Frag swz_frag_rows(const uint16_t* base, int row0, int k0) {
+  const int l = lane_id();
+  Frag f;
+  f.v = *reinterpret_cast<const u32x4*>(base + swz_off<D>(row0 + (l & 31), k0 + ((l >> 5) << 3)));
+  return f;
+}
+
+// lds_frag_cols() on a swizzled tile (each 8-byte transposing read stays inside a chunk).
+template <int D>
+__device__ __forceinline__ Frag swz_frag_cols(const uint16_t* base, int krow0, int m0) {
+  const int l = lane_id();
+  const int h = l >> 5;
+  const int col = m0 + (((l >> 4) & 1) << 4) + ((l & 3) << 2);
+  const int row = krow0 + 4 * h + ((l & 15) >> 2);
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + swz_off<D>(row, col)));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + swz_off<D>(row + 8, col)));
+  Frag f;
+  u32x2 ua = __builtin_bit_cast(u32x2, a);
+  u32x2 ub = __builtin_bit_cast(u32x2, b);
+  f.v[0] = ua[0];
+  f.v[1] = ua[1];
+  f.v[2] = ub[0];
+  f.v[3] = ub[1];
+  return f;
+}
+
+// ---------------------------------------------------------------------------------------
+// Workgroup -> (head, tile) mapping that keeps a head's tiles on one XCD.
+// The dispatcher deals workgroups round-robin over the 8 XCDs (blockIdx.x % 8), and each
+// XCD has its own L2. Renumbering so that the workgroups one XCD receives in a row are the
+// consecutive tiles of the same head lets the tiles of a head that run together share its
+// K/V (or Q/dO) reads in that XCD's L2 instead of each XCD cycling through every head.
+// `total` = number of workgroups; returns the logical index in [0, total), head-major.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_local_index(int bid, int total) {
+  const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  const int per = total / kNumXcd, rem = total % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
 // Global 16-byte load of 8 elements (zero when !valid).

@@ -27,8 +27,11 @@
 
 namespace fa {
 
+// Largest tolerated excess of a tile's max over the reference max, in log2 units: p <= 2^8.
+constexpr float kTau = 8.0f;
+
 template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, int n_qtiles, float c_log2) {
   constexpr int BM = NW * QB * 32;     // query rows per workgroup
@@ -52,12 +55,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // Heaviest causal tiles first; consecutive workgroups of one head land on one XCD
-  // (workgroups are dealt round-robin over the 8 XCDs, and BH % 8 == 0 keeps head bh on
-  // XCD bh % 8 for every Q tile), so K/V re-reads of a head hit the same L2.
-  const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int qt = CAUSAL ? (n_qtiles - 1 - bid / BH) : (bid / BH);
+  // A head's Q tiles run together on one XCD (shared K/V reads in its L2), heaviest
+  // causal tile first.
+  const int lid = xcd_local_index(blockIdx.x, BH * n_qtiles);
+  const int bh = lid / n_qtiles;
+  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * QB * 32;  // first row of this wave
 
@@ -121,11 +123,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) gload_tile(t + 1);
+    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle
+    // buffer): predicated loads would turn the staging registers into loop phis.
+    gload_tile(t + 1 < ntiles ? t + 1 : t);
     const int kbase = t * BN;
-    // Wave-uniform classification of this tile for this wave's rows.
-    const bool skip = CAUSAL && (kbase > qw0 + QB * 32 - 1);
-    if (!skip) {
+    // Every wave runs every tile of the workgroup's range (a tile entirely above this
+    // wave's rows is fully masked and adds p = 0), which keeps the loop body free of
+    // branches around the accumulators.
+    {
       const bool need_mask = (kbase + BN > N) || (CAUSAL && (kbase + BN - 1 > qw0));
       const uint16_t* ks_base = lds_k[buf];
       const uint16_t* vs_base = lds_v[buf];
@@ -164,8 +169,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
         }
       }
 
-      // ---- online softmax (base 2)
+      // ---- online softmax (base 2) with a lazily moved reference max.
+      // The reference m_ref only moves when a tile's max exceeds it by more than kTau (log2
+      // units); otherwise p = 2^(c*s - m_ref) <= 2^kTau is accumulated against the old
+      // reference. O = acc / l and LSE = ln2 * (m_ref + log2 l) are exact for any reference
+      // shared by acc and l, so this only skips rescales of the O accumulator (held in
+      // AGPRs, where each rescale costs a read-modify-write of all of it). The branch is
+      // wave-uniform: one lane that needs a move rescales the wave, with alpha = 1 for the
+      // lanes whose reference stays.
       Frag p[QB][KB][2];
+      bool moved = false;
+      float alpha[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float mx = -INFINITY;
@@ -173,11 +187,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-        mx = wave_xor32_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx * c_log2);
+        mx = wave_xor32_max(mx) * c_log2;
+        const bool move = mx > m_run[qb] + kTau;
+        const float m_new = move ? mx : m_run[qb];
+        moved |= move;
+        alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // 1 if kept, 0 from -inf
+        m_run[qb] = m_new;
         // A row that has seen no visible key keeps m = -inf; use 0 as the reference then.
         const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_ref);
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -187,17 +204,20 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
             s[qb][kb][i] = e;
             rs += e;
           }
-        l_run[qb] = l_run[qb] * alpha + rs;
-        m_run[qb] = m_new;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
+        l_run[qb] = l_run[qb] * alpha[qb] + rs;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           p[qb][kb][0] = pack_group<T>(s[qb][kb], 0);
           p[qb][kb][1] = pack_group<T>(s[qb][kb], 1);
         }
+      }
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha[qb];
       }
 
       // ---- O^T += V^T P^T
@@ -212,7 +232,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
             for (int qb = 0; qb < QB; ++qb) acc[qb][db] = T::mfma(a, p[qb][kb][tt], acc[qb][db]);
           }
     }
-    if (t + 1 < ntiles) lds_store_tile(buf ^ 1);
+    lds_store_tile(buf ^ 1);
     __syncthreads();
   }
 
@@ -240,7 +260,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  constexpr int NW = 4, QB = 2, BN = 64;
+  constexpr int NW = 4, QB = 1, BN = 64;
   constexpr int BM = NW * QB * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
   const long long grid = (long long)n_qtiles * a.BH;
