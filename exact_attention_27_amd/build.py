@@ -17,7 +17,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
 RESOURCES = os.path.join(HERE, "kernel_resources.txt")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
 
@@ -28,27 +27,50 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libfa.so")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+# Per-source extra flags. MFMA results go to VGPRs: the kernels feed S and dP straight to
+# VALU softmax code, and AGPR-destination MFMAs made the allocator shuttle accumulators
+# between the two register files on every loop iteration.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCES = {
+    "fa_api.cpp": [],
+    "fa_fwd.hip": VGPR_FORM,
+    "fa_bwd.hip": VGPR_FORM,
+    "fa_bwd_dkv.hip": VGPR_FORM,
+}
+
+
+def _common(cc):
+    return [
+        cc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Wall", "-Wno-unused-function",
         # Keep the compiler from forming packed fp32 VALU instructions.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # Give MFMA results VGPR destinations: the kernels feed S and dP straight to VALU
-        # softmax code, and AGPR-destination MFMAs made the allocator shuttle accumulators
-        # between the two register files on every loop iteration.
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-        "-Rpass-analysis=kernel-resource-usage",
         "-I", os.path.join(os.path.dirname(HERE), "include"),
-        "-o", LIB + ".tmp",
-    ] + [os.path.join(CSRC, s) for s in SOURCES]
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    report = [ln for ln in proc.stderr.splitlines() if "remark:" in ln]
-    other = [ln for ln in proc.stderr.splitlines()
-             if "remark:" not in ln and "packed-fp32-ops" not in ln and ln.strip()]
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    cc = hipcc()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    report, other, objs = [], [], []
+    for src, extra in SOURCES.items():
+        obj = os.path.join(objdir, src + ".o")
+        cmd = _common(cc) + extra + ["-Rpass-analysis=kernel-resource-usage", "-c",
+                                      os.path.join(CSRC, src), "-o", obj]
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        report += [ln for ln in proc.stderr.splitlines() if "remark:" in ln]
+        other += [ln for ln in proc.stderr.splitlines()
+                  if "remark:" not in ln and "packed-fp32-ops" not in ln and ln.strip()]
+        if proc.returncode != 0:
+            sys.stderr.write("\n".join(other) + "\n")
+            raise RuntimeError(f"hipcc failed on {src} with exit code {proc.returncode}")
+        objs.append(obj)
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    proc = subprocess.run(link, capture_output=True, text=True)
     if proc.returncode != 0:
-        sys.stderr.write("\n".join(other) + "\n")
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+        sys.stderr.write(proc.stderr)
+        raise RuntimeError(f"link failed with exit code {proc.returncode}")
     os.replace(LIB + ".tmp", LIB)
     with open(RESOURCES, "w") as f:
         f.write("\n".join(_condense(report)) + "\n")

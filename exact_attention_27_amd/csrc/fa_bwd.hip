@@ -5,7 +5,7 @@
 // softmax gradient is dS = P * (dP - D) with D_i = rowsum(dO_i * O_i) computed once, and the
 // work is split so every output tile has exactly one writer:
 //   [1] preprocess : D (here `delta`) from O and dO                      -- HBM-bound
-//   [2] dK/dV      : one workgroup per K/V tile (pinned in VGPRs), loop over Q tiles
+//   [2] dK/dV      : one workgroup per K/V tile, loop over Q tiles (fa_bwd_dkv.hip)
 //                    dV += P^T dO,  dP = dO V^T,  dS = P*(dP - D),  dK += scale * dS^T Q
 //   [3] dQ         : one workgroup per Q tile (pinned in VGPRs), loop over K/V tiles
 //                    dP = dO V^T,  dS = P*(dP - D),  dQ += scale * dS K
@@ -14,6 +14,8 @@
 // down the rows of a staged tile (Q^T, dO^T, K^T) are read with the transposing LDS load.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
+
+#include <type_traits>
 
 namespace fa {
 
@@ -40,199 +42,6 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (sub == 0) delta[row] = s;
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// [2] dK, dV. Workgroup = NW waves, each owning 32 keys; Q/dO tiles of BQ rows stream
-// through a double-buffered LDS ring together with their LSE and D values.
-template <typename T, int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, float c_log2) {
-  constexpr int BK = NW * 32;
-  constexpr int QBS = BQ / 32;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int NT = NW * 64;
-  constexpr int CHUNKS = BQ * D / 8;
-  static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly over the workgroup");
-  constexpr int CPT = CHUNKS / NT;
-  constexpr int CPR = D / 8;
-  static_assert(NT >= 2 * BQ, "LSE and D staging needs 2*BQ threads");
-
-  // Q and dO tiles are read both by rows and transposed: swizzled layout.
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float lds_lse[2][BQ];
-  __shared__ __attribute__((aligned(16))) float lds_dl[2][BQ];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-
-  // A head's K tiles run together on one XCD (shared Q/dO reads in its L2); causal: low
-  // key tiles see the most queries and go first.
-  const int n_ktiles = (N + BK - 1) / BK;
-  const int lid = xcd_local_index(blockIdx.x, BH * n_ktiles);
-  const int bh = lid / n_ktiles;
-  const int kt = lid % n_ktiles;
-  const int k0 = kt * BK;
-  const int kw0 = k0 + wave * 32;
-
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* dOh = dO + head;
-  const float* lse_h = LSE + (size_t)bh * N;
-  const float* dl_h = Delta + (size_t)bh * N;
-
-  // Pinned K and V fragments (B operands of S = Q K^T and dP = dO V^T).
-  Frag kf[KS], vf[KS];
-  {
-    const int key = kw0 + l32;
-    const bool ok = key < N;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks].v = gload16(K + head + (size_t)key * D + ks * 16 + h * 8, ok);
-      vf[ks].v = gload16(V + head + (size_t)key * D + ks * 16 + h * 8, ok);
-    }
-  }
-
-  f32x16 acc_dk[DB], acc_dv[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acc_dk[db][i] = 0.f;
-      acc_dv[db][i] = 0.f;
-    }
-
-  const int it_begin = CAUSAL ? (k0 / BQ) : 0;
-  const int it_end = (N + BQ - 1) / BQ;
-
-  u32x4 pq[CPT], pdo[CPT];
-  float pstat = 0.f;
-  auto gload_tile = [&](int it) {
-    const int qbase = it * BQ;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const bool ok = qbase + row < N;
-      pq[i] = gload16(Qh + (size_t)(qbase + row) * D + col, ok);
-      pdo[i] = gload16(dOh + (size_t)(qbase + row) * D + col, ok);
-    }
-    if (tid < BQ) {
-      const int r = qbase + tid;
-      // LSE in base 2; rows past the end get +inf so that P = 2^(-inf) = 0 there.
-      pstat = (r < N) ? lse_h[r] * kLog2e : INFINITY;
-    } else if (tid < 2 * BQ) {
-      const int r = qbase + tid - BQ;
-      pstat = (r < N) ? dl_h[r] : 0.f;
-    }
-  };
-  auto lds_store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&lds_q[buf][swz_off<D>(row, col)]) = pq[i];
-      *reinterpret_cast<u32x4*>(&lds_do[buf][swz_off<D>(row, col)]) = pdo[i];
-    }
-    if (tid < BQ) lds_lse[buf][tid] = pstat;
-    else if (tid < 2 * BQ) lds_dl[buf][tid - BQ] = pstat;
-  };
-
-  if (it_begin < it_end) {
-    gload_tile(it_begin);
-    lds_store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = it_begin; it < it_end; ++it) {
-    const int buf = (it - it_begin) & 1;
-    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle
-    // buffer): predicated loads would turn the staging registers into loop phis.
-    gload_tile(it + 1 < it_end ? it + 1 : it);
-    const int qbase = it * BQ;
-    // Every wave runs every Q tile of the workgroup's range: a tile entirely before this
-    // wave's keys is fully masked (P = 0), which keeps the loop body free of branches
-    // around the accumulators.
-    {
-      const bool need_mask = (kw0 + 31 >= N) || (CAUSAL && kw0 + 31 > qbase);
-      const uint16_t* qs = lds_q[buf];
-      const uint16_t* dos = lds_do[buf];
-      const int key = kw0 + l32;
-      Frag pf[QBS][2], dsf[QBS][2];
-#pragma unroll
-      for (int qb = 0; qb < QBS; ++qb) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[i] = 0.f;
-          dp[i] = 0.f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = T::mfma(swz_frag_rows<D>(qs, qb * 32, ks * 16), kf[ks], s);
-          dp = T::mfma(swz_frag_rows<D>(dos, qb * 32, ks * 16), vf[ks], dp);
-        }
-        // rows of this lane: q_local = 32qb + 8g + 4h + r, i = 4g + r
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ql = qb * 32 + 8 * g + 4 * h;
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lds_lse[buf][ql]);
-          const f32x4 dl4 = *reinterpret_cast<const f32x4*>(&lds_dl[buf][ql]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g + r;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -lse4[r]));
-            if (need_mask) {
-              const int qrow = qbase + ql + r;
-              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-            }
-            s[i] = p;
-            dp[i] = p * (dp[i] - dl4[r]);
-          }
-        }
-        pf[qb][0] = pack_group<T>(s, 0);
-        pf[qb][1] = pack_group<T>(s, 1);
-        dsf[qb][0] = pack_group<T>(dp, 0);
-        dsf[qb][1] = pack_group<T>(dp, 1);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QBS; ++qb)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            acc_dv[db] = T::mfma(swz_frag_cols<D>(dos, qb * 32 + tt * 16, db * 32), pf[qb][tt], acc_dv[db]);
-            acc_dk[db] = T::mfma(swz_frag_cols<D>(qs, qb * 32 + tt * 16, db * 32), dsf[qb][tt], acc_dk[db]);
-          }
-    }
-    lds_store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  const int key = kw0 + l32;
-  if (key < N) {
-    uint16_t* dk_row = dK + head + (size_t)key * D;
-    uint16_t* dv_row = dV + head + (size_t)key * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 wk, wv;
-        wk[0] = T::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale);
-        wk[1] = T::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale);
-        wv[0] = T::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]);
-        wv[1] = T::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3]);
-        *reinterpret_cast<u32x2*>(dk_row + db * 32 + 8 * g + 4 * h) = wk;
-        *reinterpret_cast<u32x2*>(dv_row + db * 32 + 8 * g + 4 * h) = wv;
-      }
   }
 }
 
@@ -428,19 +237,6 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
 }
 
 template <typename T, int D, bool CAUSAL>
-static hipError_t launch_dkv_t(const BwdArgs& a) {
-  constexpr int NW = 4, BQ = 32;
-  constexpr int BK = NW * 32;
-  const int n_ktiles = (a.N + BK - 1) / BK;
-  const long long grid = (long long)n_ktiles * a.BH;
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, BQ, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.BH, a.N, a.scale,
-                     a.c_log2);
-  return hipGetLastError();
-}
-
-template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a) {
   constexpr int NW = 4, QB = 1, BN = 32;
   constexpr int BM = NW * QB * 32;
@@ -458,18 +254,12 @@ static hipError_t pre_dt(const BwdArgs& a) {
   return a.d == 64 ? launch_pre_t<T, 64>(a) : launch_pre_t<T, 128>(a);
 }
 template <typename T>
-static hipError_t dkv_dt(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_dkv_t<T, 64, true>(a) : launch_dkv_t<T, 64, false>(a);
-  return a.causal ? launch_dkv_t<T, 128, true>(a) : launch_dkv_t<T, 128, false>(a);
-}
-template <typename T>
 static hipError_t dq_dt(const BwdArgs& a) {
   if (a.d == 64) return a.causal ? launch_dq_t<T, 64, true>(a) : launch_dq_t<T, 64, false>(a);
   return a.causal ? launch_dq_t<T, 128, true>(a) : launch_dq_t<T, 128, false>(a);
 }
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a) { return a.bf16 ? pre_dt<BF16>(a) : pre_dt<FP16>(a); }
-hipError_t launch_bwd_dkv(const BwdArgs& a) { return a.bf16 ? dkv_dt<BF16>(a) : dkv_dt<FP16>(a); }
 hipError_t launch_bwd_dq(const BwdArgs& a) { return a.bf16 ? dq_dt<BF16>(a) : dq_dt<FP16>(a); }
 
 }  // namespace fa

@@ -185,6 +185,79 @@ __device__ __forceinline__ int xcd_local_index(int bid, int total) {
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// Per-lane base offsets into a swizzled tile, from which every fragment address follows by
+// an XOR with a compile-time constant (the swizzle is linear over XOR) plus a constant add:
+//  * row reads at (row0 + l32, chunk 2ks + h): element offset = rows_base(row0) ^ (ks << 4);
+//  * transposing reads at rows krow0 + 4h + (l&15)/4 (+8), columns m0 + 16((l>>4)&1) + 4(l&3),
+//    krow0 % 16 == 0, m0 % 32 == 0: first read cols_base + krow0*D ^ ((m0/32) << 5); the
+//    second (8 rows down) flips swizzle bit 1 (element bit 4) and adds 8 rows.
+// Valid because swz(r + 16) = swz(r), swz(r + 8) = swz(r) ^ 2, and chunk bits added by ks and
+// m0 never overlap the bits h, (l>>4)&1 and (l&3)>>1 occupy.
+template <int D>
+__device__ __forceinline__ int swz_rows_base(int row0) {
+  const int l = lane_id();
+  return swz_off<D>(row0 + (l & 31), (l >> 5) << 3);
+}
+template <int D>
+__device__ __forceinline__ int swz_cols_base() {
+  const int l = lane_id();
+  return swz_off<D>(4 * (l >> 5) + ((l & 15) >> 2), (((l >> 4) & 1) << 4) + ((l & 3) << 2));
+}
+template <int D>
+__device__ __forceinline__ Frag swz_rows_frag(const uint16_t* tile, int base, int ks) {
+  Frag f;
+  f.v = *reinterpret_cast<const u32x4*>(tile + (base ^ (ks << 4)));
+  return f;
+}
+template <int D>
+__device__ __forceinline__ Frag swz_cols_frag(const uint16_t* tile, int base, int krow0, int m0) {
+  const int o0 = (base ^ ((m0 >> 5) << 5)) + krow0 * D;
+  const int o1 = (o0 ^ 16) + 8 * D;
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(tile + o0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(tile + o1));
+  Frag f;
+  u32x2 ua = __builtin_bit_cast(u32x2, a);
+  u32x2 ub = __builtin_bit_cast(u32x2, b);
+  f.v[0] = ua[0];
+  f.v[1] = ua[1];
+  f.v[2] = ub[0];
+  f.v[3] = ub[1];
+  return f;
+}
+
+// ---------------------------------------------------------------------------------------
+// Asynchronous global -> LDS staging (global_load_lds_dwordx4): one wave instruction copies
+// 64 x 16 bytes into LDS bytes [base, base + 1024), lane i landing at base + 16 i, with no
+// VGPR round trip; completion is tracked by vmcnt. wait_async() + a barrier publishes the data.
+//
+// Stage `rows` rows of D 16-bit elements starting at global row `grow0` of a head into a
+// swizzled tile. Rows at or past `n_rows` read row n_rows - 1 instead (finite data that the
+// kernels mask), so no load leaves the tensor. Waves `wave`, `wave + nw`, ... split the work.
+template <int D>
+__device__ __forceinline__ void stage_rows_swz(uint16_t* tile, const uint16_t* head, int grow0, int rows, int n_rows,
+                                               int wave, int nw) {
+  constexpr int ROW_BYTES = D * 2;
+  const int l = lane_id();
+  const int n_inst = rows * ROW_BYTES / 1024;
+  for (int ins = wave; ins < n_inst; ins += nw) {
+    const int p = ins * 1024 + l * 16;
+    const int row = p / ROW_BYTES;
+    const int lchunk = ((p % ROW_BYTES) >> 4) ^ swz<D>(row);
+    const int grow = min(grow0 + row, n_rows - 1);
+    __builtin_amdgcn_global_load_lds(head + (size_t)grow * D + lchunk * 8, tile + ins * 512, 16, 0, 0);
+  }
+}
+
+// Stage 64 floats: lanes 0..31 from a[r0 + i], lanes 32..63 from b[r0 + i - 32] (rows clamped
+// to n_rows - 1), into dst[0..63] (one wave instruction).
+__device__ __forceinline__ void stage_stats(float* dst, const float* a, const float* b, int r0, int n_rows) {
+  const int l = lane_id();
+  const int r = min(r0 + (l & 31), n_rows - 1);
+  __builtin_amdgcn_global_load_lds((l < 32 ? a : b) + r, dst, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Global 16-byte load of 8 elements (zero when !valid).
 __device__ __forceinline__ u32x4 gload16(const uint16_t* p, bool valid) {
   u32x4 z = {0u, 0u, 0u, 0u};
