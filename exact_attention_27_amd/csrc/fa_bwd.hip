@@ -46,10 +46,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
 }
 
 // ------------------------------------------------------------------------------------------
-// [3] dQ. Workgroup = NW waves, each owning QB*32 query rows (Q, dO, LSE, D pinned);
-// K/V tiles of BN keys stream through a double-buffered LDS ring.
+// [3] dQ. Workgroup = NW waves, each owning QB*32 query rows (Q, dO, LSE, D pinned); K/V
+// tiles of BN keys are copied global -> LDS (swizzled) by the asynchronous loads into a
+// double-buffered ring.
 template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, int BH, int N, int n_qtiles, float scale, float c_log2) {
@@ -57,15 +58,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int KB = BN / 32;
-  constexpr int NT = NW * 64;
-  constexpr int CHUNKS = BN * D / 8;
-  static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly over the workgroup");
-  constexpr int CPT = CHUNKS / NT;
-  constexpr int CPR = D / 8;
 
   // K is read by rows (S^T) and transposed (dQ), V by rows: swizzled layout for both.
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,6 +80,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
+
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  auto stage = [&](int t, int buf) {
+    stage_rows_swz<D>(lds_k[buf], Kh, t * BN, BN, N, wave, NW);
+    stage_rows_swz<D>(lds_v[buf], Vh, t * BN, BN, N, wave, NW);
+  };
+  stage(0, 0);
 
   Frag qf[QB][KS], dof[QB][KS];
   float lse2[QB], dl[QB];
@@ -108,99 +112,76 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  // Per-lane fragment base offsets (every fragment address is one XOR / add away).
+  const int rows0 = swz_rows_base<D>(0);
+  const int cols0 = swz_cols_base<D>();
 
-  u32x4 pk[CPT], pv[CPT];
-  auto gload_tile = [&](int t) {
-    const int kbase = t * BN;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const bool ok = kbase + row < N;
-      pk[i] = gload16(Kh + (size_t)(kbase + row) * D + col, ok);
-      pv[i] = gload16(Vh + (size_t)(kbase + row) * D + col, ok);
-    }
-  };
-  auto lds_store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&lds_k[buf][swz_off<D>(row, col)]) = pk[i];
-      *reinterpret_cast<u32x4*>(&lds_v[buf][swz_off<D>(row, col)]) = pv[i];
-    }
-  };
-
-  gload_tile(0);
-  lds_store_tile(0);
+  wait_async();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle
-    // buffer): predicated loads would turn the staging registers into loop phis.
-    gload_tile(t + 1 < ntiles ? t + 1 : t);
+    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle buffer).
+    stage(t + 1 < ntiles ? t + 1 : t, buf ^ 1);
     const int kbase = t * BN;
     // Every wave runs every K/V tile of the workgroup's range (fully masked tiles add 0).
-    {
-      const bool need_mask = (kbase + BN > N) || (CAUSAL && (kbase + BN - 1 > qw0));
-      const uint16_t* ks_base = lds_k[buf];
-      const uint16_t* vs_base = lds_v[buf];
-      f32x16 s[QB][KB], dp[QB][KB];
+    const bool need_mask = (kbase + BN > N) || (CAUSAL && (kbase + BN - 1 > qw0));
+    const uint16_t* ks_base = lds_k[buf];
+    const uint16_t* vs_base = lds_v[buf];
+    f32x16 s[QB][KB], dp[QB][KB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[qb][kb][i] = 0.f;
-            dp[qb][kb][i] = 0.f;
-          }
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const Frag ak = swz_frag_rows<D>(ks_base, kb * 32, ks * 16);
-          const Frag av = swz_frag_rows<D>(vs_base, kb * 32, ks * 16);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            s[qb][kb] = T::mfma(ak, qf[qb][ks], s[qb][kb]);
-            dp[qb][kb] = T::mfma(av, dof[qb][ks], dp[qb][kb]);
-          }
+        for (int i = 0; i < 16; ++i) {
+          s[qb][kb][i] = 0.f;
+          dp[qb][kb][i] = 0.f;
         }
-      Frag dsf[QB][KB][2];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = qw0 + qb * 32 + l32;
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+      for (int ks = 0; ks < KS; ++ks) {
+        const Frag ak = swz_rows_frag<D>(ks_base, rows0 + kb * 32 * D, ks);
+        const Frag av = swz_rows_frag<D>(vs_base, rows0 + kb * 32 * D, ks);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][i], c_log2, -lse2[qb]));
-            if (need_mask) {
-              const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-            }
-            dp[qb][kb][i] = p * (dp[qb][kb][i] - dl[qb]);
-          }
-          dsf[qb][kb][0] = pack_group<T>(dp[qb][kb], 0);
-          dsf[qb][kb][1] = pack_group<T>(dp[qb][kb], 1);
+        for (int qb = 0; qb < QB; ++qb) {
+          s[qb][kb] = T::mfma(ak, qf[qb][ks], s[qb][kb]);
+          dp[qb][kb] = T::mfma(av, dof[qb][ks], dp[qb][kb]);
         }
       }
+    Frag dsf[QB][KB][2];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = qw0 + qb * 32 + l32;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const Frag a = swz_frag_cols<D>(ks_base, kb * 32 + tt * 16, db * 32);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = T::mfma(a, dsf[qb][kb][tt], acc[qb][db]);
-          }
+        for (int i = 0; i < 16; ++i) {
+          float x = __builtin_fmaf(s[qb][kb][i], c_log2, -lse2[qb]);
+          // hidden entries get 2^-inf = 0 (a select on the exponent input, no branch)
+          const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          // (bitwise, not short-circuit, operators: keeps this a select instead of branches)
+          const bool hidden = need_mask & ((key >= N) | (CAUSAL & (key > qrow)));
+          x = hidden ? -INFINITY : x;
+          const float p = __builtin_amdgcn_exp2f(x);
+          dp[qb][kb][i] = p * (dp[qb][kb][i] - dl[qb]);
+        }
+        dsf[qb][kb][0] = pack_group<T>(dp[qb][kb], 0);
+        dsf[qb][kb][1] = pack_group<T>(dp[qb][kb], 1);
+      }
     }
-    lds_store_tile(buf ^ 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const Frag a = swz_cols_frag<D>(ks_base, cols0, kb * 32 + tt * 16, db * 32);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = T::mfma(a, dsf[qb][kb][tt], acc[qb][db]);
+        }
+    wait_async();
     __syncthreads();
   }
 
@@ -238,7 +219,7 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a) {
-  constexpr int NW = 4, QB = 1, BN = 32;
+  constexpr int NW = 4, QB = 1, BN = (D == 128) ? 64 : 32;
   constexpr int BM = NW * QB * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
   const long long grid = (long long)n_qtiles * a.BH;

@@ -130,7 +130,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
         if (MASK) {
           // hidden entries get 2^-inf = 0 (a select on the exponent input, no branch)
           const int qrow = qbase + ql + r;
-          x = (qrow >= N || key >= N || (CAUSAL && key > qrow)) ? -INFINITY : x;
+          const bool hidden = (qrow >= N) | (key >= N) | (CAUSAL & (key > qrow));
+          x = hidden ? -INFINITY : x;
         }
         const float p = __builtin_amdgcn_exp2f(x);
         s[i] = p;
