@@ -10,7 +10,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_kernels.hpp"
 
 namespace {

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
 // [3] dQ. Workgroup = NW waves, each owning QB*32 query rows (Q, dO, LSE, D pinned); K/V
 // tiles of BN keys are copied global -> LDS (swizzled) by the asynchronous loads into a
 // double-buffered ring.
-template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
+template <typename T, int D, int BN, int NW, int QB, int NBUF, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
@@ -60,8 +60,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   constexpr int KB = BN / 32;
 
   // K is read by rows (S^T) and transposed (dQ), V by rows: swizzled layout for both.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k[2][BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v[2][BN * D];
+  // One array per ring slot: with every slot index a compile-time constant the compiler can
+  // tell a copy into one slot from reads of another and does not wait for the copy first.
+  static_assert(NBUF == 2, "ring of two slots");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -83,11 +88,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
-  auto stage = [&](int t, int buf) {
-    stage_rows_swz<D>(lds_k[buf], Kh, t * BN, BN, N, wave, NW);
-    stage_rows_swz<D>(lds_v[buf], Vh, t * BN, BN, N, wave, NW);
+  auto stage = [&](int t, uint16_t* kdst, uint16_t* vdst) {
+    stage_rows_swz<D, BN, NW>(kdst, Kh, t * BN, N, wave);
+    stage_rows_swz<D, BN, NW>(vdst, Vh, t * BN, N, wave);
   };
-  stage(0, 0);
+  stage(0, lds_k0, lds_v0);
 
   Frag qf[QB][KS], dof[QB][KS];
   float lse2[QB], dl[QB];
@@ -119,15 +124,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   wait_async();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle buffer).
-    stage(t + 1 < ntiles ? t + 1 : t, buf ^ 1);
+  // One K/V tile per call; `ks_base`/`vs_base` hold tile t, the other slot receives tile
+  // t+1 (clamped: the prefetch is unconditional).
+  auto tile_step = [&](int t, const uint16_t* ks_base, const uint16_t* vs_base, uint16_t* knext,
+                       uint16_t* vnext) {
+    stage(min(t + 1, ntiles - 1), knext, vnext);
     const int kbase = t * BN;
-    // Every wave runs every K/V tile of the workgroup's range (fully masked tiles add 0).
+    // Every wave runs every K/V tile of the workgroup's range (fully masked tiles add 0;
+    // that includes the padding step when the tile count is odd).
     const bool need_mask = (kbase + BN > N) || (CAUSAL && (kbase + BN - 1 > qw0));
-    const uint16_t* ks_base = lds_k[buf];
-    const uint16_t* vs_base = lds_v[buf];
     f32x16 s[QB][KB], dp[QB][KB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -181,9 +186,19 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) acc[qb][db] = T::mfma(a, dsf[qb][kb][tt], acc[qb][db]);
         }
+    // Tile t+1 must have landed: allow the NBUF-2 younger tiles to stay in flight.
+    // Tile t+1 must have landed before anyone reads it.
     wait_async();
-    __syncthreads();
+    ring_barrier();
+  };
+  // Two steps per trip with the slots fixed at compile time; an odd tile count gets one
+  // fully masked padding step (its keys are past the causal range or past N).
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, lds_k0, lds_v0, lds_k1, lds_v1);
+    tile_step(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
   }
+  // No copy may still be landing in LDS when the workgroup retires.
+  wait_async();
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -219,11 +234,11 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a) {
-  constexpr int NW = 4, QB = 1, BN = (D == 128) ? 64 : 32;
+  constexpr int NW = 4, QB = 1, BN = 32, NBUF = 2;
   constexpr int BM = NW * QB * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
   const long long grid = (long long)n_qtiles * a.BH;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW, QB, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW, QB, NBUF, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dq, a.BH, a.N, n_qtiles, a.scale,
                      a.c_log2);

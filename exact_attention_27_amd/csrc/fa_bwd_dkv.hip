@@ -69,12 +69,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   const int it_end = (N + BQ - 1) / BQ;
 
   auto stage = [&](int it, int buf) {
-    stage_rows_swz<D>(lds_q[buf], Qh, it * BQ, BQ, N, wave, NW);
-    stage_rows_swz<D>(lds_do[buf], dOh, it * BQ, BQ, N, wave, NW);
+    stage_rows_swz<D, BQ, NW>(lds_q[buf], Qh, it * BQ, N, wave);
+    stage_rows_swz<D, BQ, NW>(lds_do[buf], dOh, it * BQ, N, wave);
     if (wave == NW - 1) stage_stats(lds_stat[buf], lse_h, dl_h, it * BQ, N);
   };
 
-  stage_rows_swz<D>(lds_v, V + head, k0, BK, N, wave, NW);
+  stage_rows_swz<D, BK, NW>(lds_v, V + head, k0, N, wave);
   stage(it_begin, 0);
 
   // Pinned K fragments (B operand of S = Q K^T): lane holds K[key][16ks + 8h .. +7].

@@ -233,13 +233,18 @@ __device__ __forceinline__ Frag swz_cols_frag(const uint16_t* tile, int base, in
 // Stage `rows` rows of D 16-bit elements starting at global row `grow0` of a head into a
 // swizzled tile. Rows at or past `n_rows` read row n_rows - 1 instead (finite data that the
 // kernels mask), so no load leaves the tensor. Waves `wave`, `wave + nw`, ... split the work.
-template <int D>
-__device__ __forceinline__ void stage_rows_swz(uint16_t* tile, const uint16_t* head, int grow0, int rows, int n_rows,
-                                               int wave, int nw) {
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void stage_rows_swz(uint16_t* tile, const uint16_t* head, int grow0, int n_rows,
+                                               int wave) {
   constexpr int ROW_BYTES = D * 2;
+  constexpr int N_INST = ROWS * ROW_BYTES / 1024;
+  // Every wave issues the same, compile-time number of copies, so the compiler's vmcnt
+  // bookkeeping is exact (it then waits only for the copies a read actually depends on).
+  static_assert(N_INST % NW == 0, "tile copies must split evenly over the waves");
   const int l = lane_id();
-  const int n_inst = rows * ROW_BYTES / 1024;
-  for (int ins = wave; ins < n_inst; ins += nw) {
+#pragma unroll
+  for (int k = 0; k < N_INST / NW; ++k) {
+    const int ins = wave + k * NW;
     const int p = ins * 1024 + l * 16;
     const int row = p / ROW_BYTES;
     const int lchunk = ((p % ROW_BYTES) >> 4) ^ swz<D>(row);
@@ -256,7 +261,20 @@ __device__ __forceinline__ void stage_stats(float* dst, const float* a, const fl
   __builtin_amdgcn_global_load_lds((l < 32 ? a : b) + r, dst, 4, 0, 0);
 }
 
-__device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) through the builtin rather than inline asm, so the compiler's wait-insertion pass
+// knows every copy has completed (immediate: vmcnt 0, expcnt 7, lgkmcnt 15).
+__device__ __forceinline__ void wait_async() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier for loops that keep asynchronous LDS copies in flight across it.
+// __syncthreads() carries a workgroup release fence, which makes the compiler wait for every
+// outstanding copy (vmcnt(0)) first; here the caller waits for exactly the copies the next
+// iteration reads, and only this wave's own LDS reads must have completed (lgkmcnt(0)) so no
+// other wave's copy can overwrite data still being read.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Global 16-byte load of 8 elements (zero when !valid).
 __device__ __forceinline__ u32x4 gload16(const uint16_t* p, bool valid) {
