@@ -171,6 +171,30 @@ __device__ __forceinline__ Frag swz_frag_cols(const uint16_t* base, int krow0, i
   return f;
 }
 
+// Fragment reads at per-lane byte offsets that already carry every XOR term of the swizzle
+// (precomputed from swz_rows_base / swz_cols_base below); what is left of the address is a
+// compile-time add that lands in the instruction's offset field, so a read costs no VALU.
+__device__ __forceinline__ Frag lds_read_rows(const uint16_t* tile, int ofs) {
+  Frag f;
+  f.v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(tile) + ofs);
+  return f;
+}
+// Transposing read pair: the first 8-byte read at ofs0 (rows krow0 + 4h + (l&15)/4), the second
+// at ofs1 (8 rows further down).
+__device__ __forceinline__ Frag lds_read_cols(const uint16_t* tile, int ofs0, int ofs1) {
+  const char* b = reinterpret_cast<const char*>(tile);
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + ofs0));
+  i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(b + ofs1));
+  Frag f;
+  u32x2 ua = __builtin_bit_cast(u32x2, a);
+  u32x2 uc = __builtin_bit_cast(u32x2, c);
+  f.v[0] = ua[0];
+  f.v[1] = ua[1];
+  f.v[2] = uc[0];
+  f.v[3] = uc[1];
+  return f;
+}
+
 // ---------------------------------------------------------------------------------------
 // Workgroup -> (head, tile) mapping that keeps a head's tiles on one XCD.
 // The dispatcher deals workgroups round-robin over the 8 XCDs (blockIdx.x % 8), and each
@@ -253,6 +277,46 @@ __device__ __forceinline__ void stage_rows_swz(uint16_t* tile, const uint16_t* h
   }
 }
 
+// The same copy through buffer_load_dwordx4 ... lds (MUBUF) instead of the FLAT-encoded
+// global_load_lds. While a FLAT instruction that may touch LDS is in flight, the compiler's
+// wait insertion cannot tell its LDS side from ordinary LDS reads and waits for lgkmcnt(0)
+// before every LDS operand use, which serialises read-ahead LDS fragment loads; the MUBUF copy
+// is counted on vmcnt only. The descriptor covers just the rows that exist: rows at or past
+// `n_rows` read as zero (hardware range check), finite data that the kernels mask.
+// Word 3 of the descriptor (0x00020000) is the gfx9 setting for untyped 32-bit access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// Descriptor of the rows [grow0, grow0 + ROWS) of a head that exist (n_rows rows in all).
+template <int D, int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* head, int grow0, int n_rows) {
+  // (readfirstlane: the value is wave-uniform; keeping it in an SGPR keeps the descriptor
+  // scalar, which the buffer instruction requires)
+  const int avail = __builtin_amdgcn_readfirstlane(max(0, min(n_rows - grow0, ROWS)));
+  return make_rsrc(head + (size_t)grow0 * D, avail * D * 2);
+}
+// Copy k (0 <= k < ROWS*D*2/1024/NW) of wave `wave`'s share of a ROWS-row tile: 1 KB, i.e.
+// 1024/(2D) whole rows, landing swizzled at tile[ins * 512 ...], ins = wave + k*NW.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void stage_copy(uint16_t* tile, __amdgpu_buffer_rsrc_t rsrc, int wave, int k) {
+  constexpr int ROW_BYTES = D * 2;
+  static_assert((ROWS * ROW_BYTES / 1024) % NW == 0, "tile copies must split evenly over the waves");
+  const int l = lane_id();
+  const int ins = wave + k * NW;
+  const int p = ins * 1024 + l * 16;
+  const int row = p / ROW_BYTES;
+  const int lchunk = ((p % ROW_BYTES) >> 4) ^ swz<D>(row);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)(tile + ins * 512), 16, row * ROW_BYTES + lchunk * 16, 0,
+                                           0, 0);
+}
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void stage_rows_swz_buf(uint16_t* tile, const uint16_t* head, int grow0, int n_rows,
+                                                   int wave) {
+  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc<D, ROWS>(head, grow0, n_rows);
+#pragma unroll
+  for (int k = 0; k < ROWS * D * 2 / 1024 / NW; ++k) stage_copy<D, ROWS, NW>(tile, rsrc, wave, k);
+}
+
 // Stage 64 floats: lanes 0..31 from a[r0 + i], lanes 32..63 from b[r0 + i - 32] (rows clamped
 // to n_rows - 1), into dst[0..63] (one wave instruction).
 __device__ __forceinline__ void stage_stats(float* dst, const float* a, const float* b, int r0, int n_rows) {
@@ -288,6 +352,29 @@ __device__ __forceinline__ float wave_xor32_max(float x) {
 __device__ __forceinline__ float wave_xor32_sum(float x) {
   return x + __shfl_xor(x, 32, 64);
 }
+
+// The same two reductions through v_permlane32_swap (a VALU op: no LDS round trip and no
+// lgkmcnt, so it does not wait behind outstanding LDS reads). Swapping x with itself leaves
+// x_l and x_(l^32) in the two results on every lane, in some order; max and sum do not care.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier (the AMDGPU backend's
+// SchedGroupMask): a sequence of group barriers tells the scheduler how to interleave
+// matrix-core, vector-ALU and LDS instructions inside one basic block.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedTrans = 0x400;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

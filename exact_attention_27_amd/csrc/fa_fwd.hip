@@ -6,10 +6,9 @@
 // 어떻게 실행되는가", sections 2-1..2-3 and 3-2).
 //
 // Work split (Q-outer, as in the FA2 walk-through, section 2-1): one workgroup per
-// (batch*head, Q tile of BM rows); each of its NW waves owns QB*32 whole query rows
-// ("split-Q", section 2-3), so row statistics never leave the wave. The K/V tiles of BN keys
-// stream through a double-buffered LDS ring: the next tile's global loads are in flight while
-// the current tile is consumed.
+// (batch*head, Q tile of BM = 32*NW rows); each of its NW waves owns 32 whole query rows
+// ("split-Q", section 2-3), so row statistics never leave the wave. K/V tiles of BN keys are
+// copied global -> LDS by the asynchronous loads (no VGPR round trip) into swizzled ring slots.
 //
 // Per K/V tile and wave:
 //   S^T = K Q^T on the matrix cores (A = K rows from LDS, B = the wave's Q held in VGPRs),
@@ -22,36 +21,44 @@
 //       in registers, round to nearest even).
 // Epilogue: divide once by l ("Triton 05", "최종 정규화"), store O and
 // LSE = ln2 * (m + log2 l).
+//
+// Software pipeline (one wave's instruction stream; both halves of a step are independent):
+//   step t:  [A] S(t+1) = K(t+1) Q^T (matrix cores)   ||  P(t) = 2^(c S(t) - m), row sums (VALU)
+//            [B] O^T += V(t)^T P(t)    (matrix cores)  ||  mask + row max of S(t+1)     (VALU)
+// so the exponentials of one tile run while the matrix cores compute the next tile's scores,
+// and the max reduction runs under the P V products. The ring staggers K one tile ahead of
+// V: step t reads K(t+1) and V(t) while the copies of K(t+2) and V(t+1) land in the slots
+// that held K(t) and V(t-1); one barrier per step publishes them.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
+
+#include <type_traits>
 
 namespace fa {
 
 // Largest tolerated excess of a tile's max over the reference max, in log2 units: p <= 2^8.
 constexpr float kTau = 8.0f;
 
-template <typename T, int D, int BN, int NW, int QB, bool CAUSAL>
+template <typename T, int D, int BN, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, int n_qtiles, float c_log2) {
-  constexpr int BM = NW * QB * 32;     // query rows per workgroup
-  constexpr int KS = D / 16;           // k-steps over the head dim
-  constexpr int DB = D / 32;           // 32-wide blocks of the head dim
-  constexpr int KB = BN / 32;          // 32-key blocks per tile
-  constexpr int SK = D + 8;            // LDS row stride of the K tile (elements)
-  constexpr int SV = D + 32;           // LDS row stride of the V tile (elements)
-  constexpr int NT = NW * 64;
-  constexpr int CHUNKS = BN * D / 8;   // 16-byte chunks per K (or V) tile
-  static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly over the workgroup");
-  constexpr int CPT = CHUNKS / NT;
-  constexpr int CPR = D / 8;           // chunks per row
+  constexpr int BM = NW * 32;  // query rows per workgroup
+  constexpr int KS = D / 16;   // k-steps over the head dim
+  constexpr int DB = D / 32;   // 32-wide blocks of the head dim
+  constexpr int KB = BN / 32;  // 32-key blocks per tile
+  static_assert(KB == 2, "the instruction interleaving below is laid out for 64-key tiles");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * SV];
+  // One array per ring slot, every slot index a compile-time constant: the compiler can then
+  // tell a copy into one slot from a read of another and does not wait for the copy first.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps copy setup scalar
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -61,210 +68,329 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   const int bh = lid / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
   const int q0 = qt * BM;
-  const int qw0 = q0 + wave * QB * 32;  // first row of this wave
+  const int qrow = q0 + wave * 32 + l32;  // this lane's query row
 
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  // Tiles [0, n_plain) have every key visible to every row of the workgroup: no mask.
+  const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
+
+  auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, N, wave); };
+  auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, N, wave); };
+  stage_k(0, lds_k0);
+  stage_v(0, lds_v0);
+  stage_k(min(1, ntiles - 1), lds_k1);
+
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qrow][16ks + 8h .. +7].
-  Frag qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qw0 + qb * 32 + l32;
+  Frag qf[KS];
+  {
     const bool ok = qrow < N;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[qb][ks].v = gload16(Qh + (size_t)qrow * D + ks * 16 + h * 8, ok);
+    for (int ks = 0; ks < KS; ++ks) qf[ks].v = gload16(Q + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
   }
 
-  f32x16 acc[QB][DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  // Row state. m_run: the reference max (log2 units, -inf before any visible key); m_ref: the
+  // same, made finite, used as the exponent offset; l_run: this lane's partial row sum (its 16
+  // keys of each 32-key block; the two halves are merged in the epilogue).
+  float m_run = -INFINITY, m_ref = 0.f, l_run = 0.f;
+  float alpha = 1.f;   // rescale factor owed by acc and l before the pending P is added
+  bool moved = false;  // this lane's reference moved for the pending tile
+
+  // Loop-invariant per-lane byte offsets of every fragment read. The swizzle is linear over
+  // XOR, so K row reads need one offset per k-step and V^T transposing reads two per 32-column
+  // block; key-block, 16-row and 8-row steps are plain adds folded into the instructions.
+  int kofs[KS], vofs[DB][2];
+  {
+    const int r0 = swz_rows_base<D>(0) * 2, c0 = swz_cols_base<D>() * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kofs[ks] = r0 ^ (ks << 5);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      vofs[db][0] = c0 ^ (db << 6);
+      vofs[db][1] = vofs[db][0] ^ 32;
+    }
+  }
+  // K fragment i = (key block i / KS, k-step i % KS); V^T fragment (d block db, keys of the
+  // 16-key group g).
+  auto kfrag = [&](const uint16_t* ktile, int i) {
+    return lds_read_rows(ktile, kofs[i % KS] + (i / KS) * 32 * D * 2);
+  };
+  auto vfrag = [&](const uint16_t* vtile, int db, int g) {
+    return lds_read_cols(vtile, vofs[db][0] + g * 16 * D * 2, vofs[db][1] + (g * 16 + 8) * D * 2);
+  };
+
+  // S^T tile (32 keys x 32 rows per block) from a K slot.
+  auto qk = [&](const uint16_t* ktile, f32x16 (&s)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = T::mfma(kfrag(ktile, kb * KS), qf[0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) s[kb] = T::mfma(kfrag(ktile, kb * KS + ks), qf[ks], s[kb]);
+    }
+  };
+  // Hide keys past N and (causal) keys after this lane's row.
+  auto mask = [&](f32x16 (&s)[KB], int t) {
+    const int kbase = t * BN;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        // bitwise, not short-circuit, operators: a select per element instead of branches
+        const bool hidden = (key >= N) | (CAUSAL & (key > qrow));
+        s[kb][i] = hidden ? -INFINITY : s[kb][i];
+      }
+  };
+  // Row max of a scores tile -> new reference (moved lazily: only when the tile's max exceeds
+  // the reference by more than kTau; otherwise p = 2^(c s - m_ref) <= 2^kTau accumulates
+  // against the old one). O = acc / l and LSE = ln2 (m_ref + log2 l) hold for any reference
+  // that acc and l share, so skipping a move only skips a rescale of acc.
+  // Tile max (this lane's scores) -> new reference, moved lazily: only when the tile's max
+  // exceeds the reference by more than kTau; otherwise p = 2^(c s - m_ref) <= 2^kTau
+  // accumulates against the old one. O = acc / l and LSE = ln2 (m_ref + log2 l) hold for any
+  // reference that acc and l share, so skipping a move only skips a rescale of acc.
+  auto update_ref = [&](float mx) {
+    mx = half_swap_max(mx) * c_log2;
+    moved = mx > m_run + kTau;
+    m_run = moved ? mx : m_run;
+    // A row that has seen no visible key keeps m_run = -inf; its reference is 0 then.
+    const float ref = (m_run == -INFINITY) ? 0.f : m_run;
+    alpha = __builtin_amdgcn_exp2f(m_ref - ref);  // 1 if kept; finite in every case
+    m_ref = ref;
+  };
+  auto row_max = [&](const f32x16 (&s)[KB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    update_ref(mx);
+  };
+  // P = 2^(c s - m_ref) packed to 16-bit B operands; l = alpha l + row sum.
+  auto softmax_p = [&](f32x16 (&s)[KB], Frag (&pf)[KB][2]) {
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c_log2, -m_ref));
+        s[kb][i] = e;
+        rs += e;
+      }
+    l_run = __builtin_fmaf(l_run, alpha, rs);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      pf[kb][0] = pack_group<T>(s[kb], 0);
+      pf[kb][1] = pack_group<T>(s[kb], 1);
+    }
+  };
+  // The rescale is owed by the whole wave when any lane's reference moved (alpha = 1 for the
+  // others); the branch is wave-uniform and rarely taken.
+  auto rescale = [&]() {
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+  };
+  auto pv = [&](const uint16_t* vtile, const Frag (&pf)[KB][2]) {
+#pragma unroll
+    for (int g = 0; g < KB * 2; ++g)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = T::mfma(vfrag(vtile, db, g), pf[g / 2][g % 2], acc[db]);
+  };
+
+  // ---- prologue: K(0), V(0), K(1) landed; S(0) and its reference.
+  wait_async();
+  __syncthreads();
+  f32x16 s[KB];
+  qk(lds_k0, s);
+  if (n_plain == 0) mask(s, 0);
+  row_max(s);
+  // Every wave is done with slot k0 before the first step copies K(2) over it.
+  ring_barrier();
+
+  // ---- steps t = 0 .. ntiles-2, slot parity P = t & 1 fixed at compile time.
+  auto step = [&](auto mask_tag, auto parity_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int P = decltype(parity_tag)::value;
+    const uint16_t* kcur = P ? lds_k0 : lds_k1;  // K(t+1)
+    const uint16_t* vcur = P ? lds_v1 : lds_v0;  // V(t)
+    uint16_t* kdst = P ? lds_k1 : lds_k0;        // K(t+2) replaces K(t)
+    uint16_t* vdst = P ? lds_v0 : lds_v1;        // V(t+1) replaces V(t-1)
+    // Copies of K(t+2) and V(t+1): descriptors now, the copies themselves spread over the
+    // chunks of [A] (issued all at once, the workgroup's waves queue behind each other in the
+    // texture unit right after the barrier).
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, min(t + 2, ntiles - 1) * BN, N);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, BN>(Vh, (t + 1) * BN, N);
+    constexpr int CPW = BN * D * 2 / 1024 / NW;  // copies per wave per tile
+
+    // [A] S(t+1) on the matrix cores while the VALU exponentiates S(t). Written out as 16
+    // chunks fenced by sched_barrier(0), so the order survives the scheduler: chunk i issues
+    // every GAP-th chunk one tile copy, the K fragment read for MFMA i+2, MFMA i (the two key
+    // blocks alternate, so consecutive MFMAs are independent), and 2 of the 32 exponentials.
+    f32x16 sn[KB];
+    {
+      constexpr int NA = KB * KS;  // MFMAs in this half
+      Frag kf[3];
+      auto kread = [&](int i) { return kfrag(kcur, (i % KB) * KS + i / KB); };
+      kf[0] = kread(0);
+      kf[1] = kread(1);
+      constexpr int GAP = NA / (2 * CPW);  // chunks between two copies
+      static_assert(GAP >= 1 && NA % (2 * CPW) == 0, "copies must spread evenly over [A]");
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        if (i % GAP == 0) {
+          const int c = i / GAP;
+          if (c < CPW)
+            stage_copy<D, BN, NW>(kdst, rk, wave, c);
+          else
+            stage_copy<D, BN, NW>(vdst, rv, wave, c - CPW);
+        }
+        if (i + 2 < NA) kf[(i + 2) % 3] = kread(i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = i % KB, ks = i / KB;
+        sn[kb] = T::mfma(kf[i % 3], qf[ks], ks == 0 ? f32x16{} : sn[kb]);
+#pragma unroll
+        for (int e = 0; e < 32 / NA; ++e) {
+          const int idx = i * (32 / NA) + e;
+          s[idx / 16][idx % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[idx / 16][idx % 16], c_log2, -m_ref));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Pin the exponentials here: otherwise the compiler sinks them below the rescale
+      // branch, next to their first use, out of reach of the MFMAs above.
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(s[kb]));
+    }
+
+    rescale();
+
+    // [B] O += P(t) V(t) on the matrix cores while the VALU finishes P(t) and reduces S(t+1):
+    // chunk j issues the V^T fragment reads for MFMA j+2, MFMA j, 4/DB 16-bit conversions of
+    // P (a group of 16 keys is converted while the previous group is in use), 2 adds of the
+    // row sum and the masked max over 2 scores of S(t+1). MFMAs run key-group-major, so the 4
+    // consecutive ones of a group hit independent accumulators.
+    {
+      constexpr int NG = KB * 2;  // 16-key groups of P
+      constexpr int NB = DB * NG;  // MFMAs in this half
+      Frag pf[NG];
+      pf[0] = pack_group<T>(s[0], 0);
+      Frag vf[3];
+      auto vread = [&](int j) { return vfrag(vcur, j % DB, j / DB); };
+      vf[0] = vread(0);
+      vf[1] = vread(1);
+      float mx = -INFINITY, rs = 0.f;
+      const int kbase = (t + 1) * BN;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (j + 2 < NB) vf[(j + 2) % 3] = vread(j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = j / DB, db = j % DB;
+        acc[db] = T::mfma(vf[j % 3], pf[g], acc[db]);
+        if (g + 1 < NG) {
+          // the next group's 4 packed pairs, 4 / DB of them per chunk
+          const int gn = g + 1;
+#pragma unroll
+          for (int c = 0; c < 4 / DB; ++c) {
+            const int w = db * (4 / DB) + c;
+            pf[gn].v[w] = T::pack2(s[gn / 2][8 * (gn % 2) + 2 * w], s[gn / 2][8 * (gn % 2) + 2 * w + 1]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 32 / NB; ++e) {
+          const int idx = j * (32 / NB) + e;
+          rs += s[idx / 16][idx % 16];
+          float x = sn[idx / 16][idx % 16];
+          if (MASK) {
+            const int i = idx % 16;
+            const int key = kbase + (idx / 16) * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            // bitwise, not short-circuit, operators: a select instead of branches
+            const bool hidden = (key >= N) | (CAUSAL & (key > qrow));
+            x = hidden ? -INFINITY : x;
+            sn[idx / 16][idx % 16] = x;
+          }
+          mx = fmaxf(mx, x);
+        }
+        asm volatile("" : "+v"(mx), "+v"(rs));  // keep both running reductions in this chunk
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run = __builtin_fmaf(l_run, alpha, rs);
+      update_ref(mx);
+    }
+
+    // K(t+2) and V(t+1) must have landed before anyone reads them.
+    wait_async();
+    ring_barrier();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
+  };
+  // ---- last tile: P and P V only.
+  auto drain = [&](auto parity_tag) {
+    constexpr int P = decltype(parity_tag)::value;
+    Frag pf[KB][2];
+    softmax_p(s, pf);
+    rescale();
+    pv(P ? lds_v1 : lds_v0, pf);
+  };
+
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  const int last = ntiles - 1;
+  // Steps whose next tile needs no mask: t + 1 < n_plain.
+  const int plain_steps = max(0, min(n_plain - 1, last));
+  int t = 0;
+  for (; t + 1 < plain_steps; t += 2) {
+    step(F(), Even(), t);
+    step(F(), Odd(), t + 1);
+  }
+  for (; t < last; t += 2) {
+    step(Tr(), Even(), t);
+    if (t + 1 < last) step(Tr(), Odd(), t + 1);
+  }
+  if (last & 1)
+    drain(Odd());
+  else
+    drain(Even());
+
+  // ---- epilogue: one division per row, store O and LSE
+  const float l_tot = half_swap_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (qrow < N) {
+    uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;  // per-lane partial sum over this lane's keys; halves merged at the end
-  }
-
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
-
-  u32x4 pk[CPT], pv[CPT];
-  auto gload_tile = [&](int t) {
-    const int kbase = t * BN;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const bool ok = kbase + row < N;
-      pk[i] = gload16(Kh + (size_t)(kbase + row) * D + col, ok);
-      pv[i] = gload16(Vh + (size_t)(kbase + row) * D + col, ok);
-    }
-  };
-  auto lds_store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(&lds_k[buf][row * SK + col]) = pk[i];
-      *reinterpret_cast<u32x4*>(&lds_v[buf][row * SV + col]) = pv[i];
-    }
-  };
-
-  gload_tile(0);
-  lds_store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    // Prefetch unconditionally (the last iteration re-reads a valid tile into the idle
-    // buffer): predicated loads would turn the staging registers into loop phis.
-    gload_tile(t + 1 < ntiles ? t + 1 : t);
-    const int kbase = t * BN;
-    // Every wave runs every tile of the workgroup's range (a tile entirely above this
-    // wave's rows is fully masked and adds p = 0), which keeps the loop body free of
-    // branches around the accumulators.
-    {
-      const bool need_mask = (kbase + BN > N) || (CAUSAL && (kbase + BN - 1 > qw0));
-      const uint16_t* ks_base = lds_k[buf];
-      const uint16_t* vs_base = lds_v[buf];
-
-      // ---- S^T = K Q^T
-      f32x16 s[QB][KB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[qb][kb][i] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Frag a = lds_frag_rows(ks_base, SK, kb * 32, ks * 16);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = T::mfma(a, qf[qb][ks], s[qb][kb]);
-        }
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = T::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
+        w[1] = T::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
       }
-
-      // ---- mask (diagonal / tail tiles only)
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qrow = qw0 + qb * 32 + l32;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-              const bool hidden = (key >= N) || (CAUSAL && key > qrow);
-              if (hidden) s[qb][kb][i] = -INFINITY;
-            }
-        }
-      }
-
-      // ---- online softmax (base 2) with a lazily moved reference max.
-      // The reference m_ref only moves when a tile's max exceeds it by more than kTau (log2
-      // units); otherwise p = 2^(c*s - m_ref) <= 2^kTau is accumulated against the old
-      // reference. O = acc / l and LSE = ln2 * (m_ref + log2 l) are exact for any reference
-      // shared by acc and l, so this only skips rescales of the O accumulator (held in
-      // AGPRs, where each rescale costs a read-modify-write of all of it). The branch is
-      // wave-uniform: one lane that needs a move rescales the wave, with alpha = 1 for the
-      // lanes whose reference stays.
-      Frag p[QB][KB][2];
-      bool moved = false;
-      float alpha[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-        mx = wave_xor32_max(mx) * c_log2;
-        const bool move = mx > m_run[qb] + kTau;
-        const float m_new = move ? mx : m_run[qb];
-        moved |= move;
-        alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // 1 if kept, 0 from -inf
-        m_run[qb] = m_new;
-        // A row that has seen no visible key keeps m = -inf; use 0 as the reference then.
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][i], c_log2, -m_ref));
-            s[qb][kb][i] = e;
-            rs += e;
-          }
-        l_run[qb] = l_run[qb] * alpha[qb] + rs;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          p[qb][kb][0] = pack_group<T>(s[qb][kb], 0);
-          p[qb][kb][1] = pack_group<T>(s[qb][kb], 1);
-        }
-      }
-      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha[qb];
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            Frag a = lds_frag_cols(vs_base, SV, kb * 32 + tt * 16, db * 32);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = T::mfma(a, p[qb][kb][tt], acc[qb][db]);
-          }
-    }
-    lds_store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: one division per row, store O and LSE
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qw0 + qb * 32 + l32;
-    const float l_tot = wave_xor32_sum(l_run[qb]);
-    const float inv = 1.0f / l_tot;
-    if (qrow < N) {
-      uint16_t* orow = O + head + (size_t)qrow * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w;
-          w[0] = T::pack2(acc[qb][db][4 * g + 0] * inv, acc[qb][db][4 * g + 1] * inv);
-          w[1] = T::pack2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
-        }
-      if (LSE != nullptr && h == 0) LSE[(size_t)bh * N + qrow] = (m_run[qb] + __log2f(l_tot)) * kLn2;
-    }
+    if (LSE != nullptr && h == 0) LSE[(size_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
   }
 }
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  constexpr int NW = 4, QB = 1, BN = 64;
-  constexpr int BM = NW * QB * 32;
+  constexpr int NW = 4, BN = 64;
+  constexpr int BM = NW * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
   const long long grid = (long long)n_qtiles * a.BH;
-  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, QB, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.BH, a.N, n_qtiles, a.c_log2);
   return hipGetLastError();
