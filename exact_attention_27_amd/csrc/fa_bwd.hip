@@ -70,15 +70,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps copy setup scalar
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
   // A head's Q tiles run together on one XCD (shared K/V reads in its L2), heaviest
   // causal tile first.
   const int lid = xcd_local_index(blockIdx.x, BH * n_qtiles);
-  const int bh = lid / n_qtiles;
-  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
+  const int bh = __builtin_amdgcn_readfirstlane(lid / n_qtiles);  // wave-uniform (keeps pointers scalar)
+  const int qt = __builtin_amdgcn_readfirstlane(CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles));
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * QB * 32;
 
@@ -89,8 +89,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
   auto stage = [&](int t, uint16_t* kdst, uint16_t* vdst) {
-    stage_rows_swz<D, BN, NW>(kdst, Kh, t * BN, N, wave);
-    stage_rows_swz<D, BN, NW>(vdst, Vh, t * BN, N, wave);
+    stage_rows_swz_buf<D, BN, NW>(kdst, Kh, t * BN, N, wave);
+    stage_rows_swz_buf<D, BN, NW>(vdst, Vh, t * BN, N, wave);
   };
   stage(0, lds_k0, lds_v0);
 

@@ -3,16 +3,19 @@
 // streams past; each workgroup owns its dK_j, dV_j, so no atomics are needed).
 //
 // Per 32-query step and wave (32 keys): S = Q K^T and dP = dO V^T on the matrix cores
-// (A = Q / dO rows from LDS, B = the wave's pinned K / V), P = 2^(c*S - LSE*log2 e) with the
-// causal / tail mask folded into the exponent input, dS = P * (dP - D), then
-// dV^T += dO^T P and dK^T += Q^T dS (A = transposing LDS reads, B = P / dS rounded to the
-// input type). dK is scaled once at the end.
+// (A = Q / dO rows from LDS, B = the wave's pinned K / its V rows from LDS),
+// P = 2^(c*S - LSE*log2 e) with the causal / tail mask folded into the exponent input,
+// dS = P * (dP - D), then dV^T += dO^T P and dK^T += Q^T dS (A = transposing LDS reads,
+// B = P / dS rounded to the input type). dK is scaled once at the end.
 //
-// Register plan (d = 128: one wave per SIMD): dK^T and dV^T accumulators (128), pinned K and
-// V fragments (64), S, dP and operands in VGPRs. The step body is a single path -- the
-// causal / tail mask is a select on the exponent input, evaluated every step -- because a
-// masked and an unmasked copy of the body made the allocator copy the accumulators at the
-// join on every iteration.
+// Instruction schedule of a step (one wave; 32 MFMAs in four phases of 8, each phase written
+// as sched_barrier-fenced chunks with the LDS fragment reads issued ahead of their MFMA):
+//   [S]  8 MFMAs S = Q K^T          || the copies of the next Q / dO tile
+//   [dP] 8 MFMAs dP = dO V^T        || P = 2^(c S - LSE log2 e) and its 16-bit packing
+//   [dV] 8 MFMAs dV^T += dO^T P     || dS = P (dP - D) and its packing
+//   [dK] 8 MFMAs dK^T += Q^T dS
+// Steps on the causal diagonal or a tail (queries past N, keys past N) run a copy of the
+// body with the mask; all others run without it.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -35,17 +38,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   constexpr int BQ = 32;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int CPW = BQ * D * 2 / 1024 / NW;  // tile copies per wave per Q (or dO) tile
+  static_assert(CPW >= 1, "each wave copies at least one KB of a tile");
 
   // The workgroup's V tile stays in LDS; Q/dO tiles stream. All tiles are swizzled (row and
-  // transposed reads are both conflict-free).
+  // transposed reads are both conflict-free). One array per ring slot, every slot index a
+  // compile-time constant: the compiler can then tell a copy into one slot from a read of
+  // another and does not wait for the copy first.
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_q[2][BQ * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_do[2][BQ * D];
-  __shared__ __attribute__((aligned(256))) float lds_stat[2][64];  // [0,32): LSE, [32,64): D
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_q0[BQ * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_q1[BQ * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_do0[BQ * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_do1[BQ * D];
+  __shared__ __attribute__((aligned(512))) float lds_st0[128];  // [0,32): LSE, [kStatB, +32): D
+  __shared__ __attribute__((aligned(512))) float lds_st1[128];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps copy setup scalar
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -53,8 +63,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   // key tiles see the most queries and go first.
   const int n_ktiles = (N + BK - 1) / BK;
   const int lid = xcd_local_index(blockIdx.x, BH * n_ktiles);
-  const int bh = lid / n_ktiles;
-  const int kt = lid % n_ktiles;
+  const int bh = __builtin_amdgcn_readfirstlane(lid / n_ktiles);  // wave-uniform (keeps
+  const int kt = __builtin_amdgcn_readfirstlane(lid % n_ktiles);  // pointers scalar)
   const int k0 = kt * BK;
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
@@ -68,14 +78,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   const int it_begin = CAUSAL ? (k0 / BQ) : 0;
   const int it_end = (N + BQ - 1) / BQ;
 
-  auto stage = [&](int it, int buf) {
-    stage_rows_swz<D, BQ, NW>(lds_q[buf], Qh, it * BQ, N, wave);
-    stage_rows_swz<D, BQ, NW>(lds_do[buf], dOh, it * BQ, N, wave);
-    if (wave == NW - 1) stage_stats(lds_stat[buf], lse_h, dl_h, it * BQ, N);
-  };
-
-  stage_rows_swz<D, BK, NW>(lds_v, V + head, k0, N, wave);
-  stage(it_begin, 0);
+  stage_rows_swz_buf<D, BK, NW>(lds_v, V + head, k0, N, wave);
+  stage_rows_swz_buf<D, BQ, NW>(lds_q0, Qh, it_begin * BQ, N, wave);
+  stage_rows_swz_buf<D, BQ, NW>(lds_do0, dOh, it_begin * BQ, N, wave);
+  if (wave == NW - 1) stage_stats_buf(lds_st0, lse_h, dl_h, it_begin * BQ, N);
 
   // Pinned K fragments (B operand of S = Q K^T): lane holds K[key][16ks + 8h .. +7].
   Frag kf[KS];
@@ -95,68 +101,170 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   wait_async();
   __syncthreads();
 
-  // Per-lane fragment base offsets (every fragment address is one XOR / add away).
-  const int rows0 = swz_rows_base<D>(0);
-  const int rows_v = swz_rows_base<D>(wave * 32);
-  const int cols0 = swz_cols_base<D>();
-
-  // One 32-query step; the mask handles the causal diagonal and the tails (q >= N, key >= N).
-  auto step = [&](auto mask_tag, int it, int buf) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const uint16_t* qs = lds_q[buf];
-    const uint16_t* dos = lds_do[buf];
-    const int qbase = it * BQ;
-    f32x16 s, dp;
+  // Loop-invariant per-lane byte offsets of every fragment read (the swizzle is linear over
+  // XOR): row reads of Q / dO / V need one offset per k-step, transposing reads of Q / dO two
+  // per 32-column block; tile bases and row steps are adds folded into the instructions.
+  int rofs[KS], cofs[DB][2];
+  {
+    const int r0 = swz_rows_base<D>(0) * 2, c0 = swz_cols_base<D>() * 2;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = 0.f;
-      dp[i] = 0.f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = T::mfma(swz_rows_frag<D>(qs, rows0, ks), kf[ks], s);
-      dp = T::mfma(swz_rows_frag<D>(dos, rows0, ks), swz_rows_frag<D>(lds_v, rows_v, ks), dp);
-    }
-    // rows of this lane: q_local = 8g + 4h + r for register i = 4g + r
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int ql = 8 * g + 4 * h;
-      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lds_stat[buf][ql]);
-      const f32x4 dl4 = *reinterpret_cast<const f32x4*>(&lds_stat[buf][32 + ql]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g + r;
-        float x = __builtin_fmaf(s[i], c_log2, -lse4[r] * kLog2e);
-        if (MASK) {
-          // hidden entries get 2^-inf = 0 (a select on the exponent input, no branch)
-          const int qrow = qbase + ql + r;
-          const bool hidden = (qrow >= N) | (key >= N) | (CAUSAL & (key > qrow));
-          x = hidden ? -INFINITY : x;
-        }
-        const float p = __builtin_amdgcn_exp2f(x);
-        s[i] = p;
-        dp[i] = p * (dp[i] - dl4[r]);
-      }
-    }
-    const Frag pf0 = pack_group<T>(s, 0), pf1 = pack_group<T>(s, 1);
-    const Frag df0 = pack_group<T>(dp, 0), df1 = pack_group<T>(dp, 1);
+    for (int ks = 0; ks < KS; ++ks) rofs[ks] = r0 ^ (ks << 5);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      acc_dv[db] = T::mfma(swz_cols_frag<D>(dos, cols0, 0, db * 32), pf0, acc_dv[db]);
-      acc_dv[db] = T::mfma(swz_cols_frag<D>(dos, cols0, 16, db * 32), pf1, acc_dv[db]);
-      acc_dk[db] = T::mfma(swz_cols_frag<D>(qs, cols0, 0, db * 32), df0, acc_dk[db]);
-      acc_dk[db] = T::mfma(swz_cols_frag<D>(qs, cols0, 16, db * 32), df1, acc_dk[db]);
+      cofs[db][0] = c0 ^ (db << 6);
+      cofs[db][1] = cofs[db][0] ^ 32;
     }
+  }
+  // Transposing fragment: rows krow0 .. krow0 + 15 (k index), columns of d block db.
+  auto tfrag = [&](const uint16_t* tile, int db, int krow0) __attribute__((always_inline)) {
+    return lds_read_cols(tile, cofs[db][0] + krow0 * D * 2, cofs[db][1] + (krow0 + 8) * D * 2);
   };
 
-  for (int it = it_begin; it < it_end; ++it) {
-    const int buf = (it - it_begin) & 1;
-    // Prefetch unconditionally (the last step re-reads a valid tile into the idle buffer).
-    stage(it + 1 < it_end ? it + 1 : it, buf ^ 1);
-    step(std::integral_constant<bool, true>(), it, buf);
+  // One 32-query step: reads slot (qs, dos, st), copies the next tile into (qn, don, stn).
+  // Register i of S / dP holds query row qbase + 8(i/4) + 4h + (i%4) and this lane's key.
+  // (always_inline: six copies of this body exceed the inliner's budget, and a call would
+  // leave the accumulators in scratch memory)
+  auto step = [&](auto mask_tag, int it, const uint16_t* qs, const uint16_t* dos, const float* st, uint16_t* qn,
+                  uint16_t* don, float* stn) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int qbase = it * BQ;
+    // this wave's V rows: base offset re-materialised each step (kept opaque so the compiler
+    // adds it per read instead of holding KS more loop-invariant addresses)
+    int vrow = wave * 32 * D * 2;
+    asm volatile("" : "+v"(vrow));
+    const int itn = min(it + 1, it_end - 1);
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc<D, BQ>(Qh, itn * BQ, N);
+    const __amdgpu_buffer_rsrc_t rdo = tile_rsrc<D, BQ>(dOh, itn * BQ, N);
+    if (wave == NW - 1) stage_stats_buf(stn, lse_h, dl_h, itn * BQ, N);
+
+    // this lane's LSE (then D) values for register group g (rows 8g + 4h .. +3), each read
+    // one group ahead of its use inside the chunks below
+    f32x4 st4[4];
+    auto st_read = [&](int base, int g) { return *reinterpret_cast<const f32x4*>(&st[base + 8 * g + 4 * h]); };
+    st4[0] = st_read(0, 0);
+
+    // ---- [S]: chunk ks issues a tile copy every GAP chunks, the Q fragment read for MFMA
+    // ks+2 and MFMA ks.
+    f32x16 s, dp;
+    {
+      constexpr int GAP = KS / (2 * CPW);
+      static_assert(GAP >= 1 && KS % (2 * CPW) == 0, "copies must spread evenly over [S]");
+      Frag qfr[3];
+      qfr[0] = lds_read_rows(qs, rofs[0]);
+      qfr[1] = lds_read_rows(qs, rofs[1]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks % GAP == 0) {
+          const int c = ks / GAP;
+          if (c < CPW)
+            stage_copy<D, BQ, NW>(qn, rq, wave, c);
+          else
+            stage_copy<D, BQ, NW>(don, rdo, wave, c - CPW);
+        }
+        if (ks + 2 < KS) qfr[(ks + 2) % 3] = lds_read_rows(qs, rofs[ks + 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        s = T::mfma(qfr[ks % 3], kf[ks], ks == 0 ? f32x16{} : s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- [dP]: chunk ks issues the dO and V fragment reads for MFMA ks+1, MFMA ks, and the
+    // exponentials (and packing) of 16/KS scores of S.
+    Frag pf[2], df[2];
+    {
+      constexpr int EPC = 16 / KS;  // elements per chunk
+      Frag dfr[2], vfr[2];
+      dfr[0] = lds_read_rows(dos, rofs[0]);
+      vfr[0] = lds_read_rows(lds_v, rofs[0] + vrow);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          dfr[(ks + 1) % 2] = lds_read_rows(dos, rofs[ks + 1]);
+          vfr[(ks + 1) % 2] = lds_read_rows(lds_v, rofs[ks + 1] + vrow);
+        }
+        if ((ks * EPC) % 4 == 0 && (ks * EPC) / 4 + 1 < 4) st4[(ks * EPC) / 4 + 1] = st_read(0, (ks * EPC) / 4 + 1);
+        if (ks == KS - 1) st4[0] = st_read(kStatB, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        dp = T::mfma(dfr[ks % 2], vfr[ks % 2], ks == 0 ? f32x16{} : dp);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const int i = ks * EPC + e;
+          float x = __builtin_fmaf(s[i], c_log2, -st4[i / 4][i % 4] * kLog2e);
+          if (MASK) {
+            // hidden entries get 2^-inf = 0 (a select on the exponent input, no branch;
+            // bitwise operators keep it a select)
+            const int qrow = qbase + 8 * (i / 4) + 4 * h + (i % 4);
+            const bool hidden = (qrow >= N) | (key >= N) | (CAUSAL & (key > qrow));
+            x = hidden ? -INFINITY : x;
+          }
+          s[i] = __builtin_amdgcn_exp2f(x);
+          if (i % 2 == 1) pf[i / 8].v[(i % 8) / 2] = T::pack2(s[i - 1], s[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- [dV]: chunk j (16-key half tt = j / DB, d block db = j % DB) issues the dO^T
+    // fragment read for MFMA j+1, MFMA j, and dS (and packing) of 16/(2 DB) elements.
+    {
+      constexpr int NJ = 2 * DB;
+      constexpr int EPC = 16 / NJ;
+      Frag tfr[2];
+      tfr[0] = tfrag(dos, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j + 1 < NJ) tfr[(j + 1) % 2] = tfrag(dos, (j + 1) % DB, ((j + 1) / DB) * 16);
+        if ((j * EPC) % 4 == 0 && (j * EPC) / 4 + 1 < 4) st4[(j * EPC) / 4 + 1] = st_read(kStatB, (j * EPC) / 4 + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        acc_dv[j % DB] = T::mfma(tfr[j % 2], pf[j / DB], acc_dv[j % DB]);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const int i = j * EPC + e;
+          dp[i] = s[i] * (dp[i] - st4[i / 4][i % 4]);
+          if (i % 2 == 1) df[i / 8].v[(i % 8) / 2] = T::pack2(dp[i - 1], dp[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- [dK]: chunk j issues the Q^T fragment read for MFMA j+1 and MFMA j.
+    {
+      constexpr int NJ = 2 * DB;
+      Frag tfr[2];
+      tfr[0] = tfrag(qs, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j + 1 < NJ) tfr[(j + 1) % 2] = tfrag(qs, (j + 1) % DB, ((j + 1) / DB) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        acc_dk[j % DB] = T::mfma(tfr[j % 2], df[j / DB], acc_dk[j % DB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // The next tile must have landed before anyone reads it.
     wait_async();
-    __syncthreads();
-  }
+    ring_barrier();
+  };
+
+  // Two steps per trip with the slots fixed at compile time. Masked steps: the causal diagonal
+  // (the first BK/BQ steps), and every step when this tile has keys past N; the plain loop
+  // takes the full query tiles after that; the masked tail takes the rest, with one fully
+  // masked padding step (queries past N) when the count is odd.
+  using F = std::false_type;
+  using Tr = std::true_type;
+  auto pair = [&](auto mask_tag, int it) __attribute__((always_inline)) {
+    step(mask_tag, it, lds_q0, lds_do0, lds_st0, lds_q1, lds_do1, lds_st1);
+    step(mask_tag, it + 1, lds_q1, lds_do1, lds_st1, lds_q0, lds_do0, lds_st0);
+  };
+  const bool key_tail = k0 + BK > N;
+  const int plain_begin = key_tail ? it_end : (CAUSAL ? min(it_begin + BK / BQ, it_end) : it_begin);
+  const int plain_end = key_tail ? it_end : max(plain_begin, N / BQ);
+  int it = it_begin;
+  for (; it < plain_begin; it += 2) pair(Tr(), it);
+  for (; it + 2 <= plain_end; it += 2) pair(F(), it);
+  for (; it < it_end; it += 2) pair(Tr(), it);
+  // No copy may still be landing in LDS when the workgroup retires.
+  wait_async();
 
   if (key < N) {
     uint16_t* dk_row = dK + head + (size_t)key * D;

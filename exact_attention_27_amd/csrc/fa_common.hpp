@@ -250,53 +250,36 @@ __device__ __forceinline__ Frag swz_cols_frag(const uint16_t* tile, int base, in
 }
 
 // ---------------------------------------------------------------------------------------
-// Asynchronous global -> LDS staging (global_load_lds_dwordx4): one wave instruction copies
-// 64 x 16 bytes into LDS bytes [base, base + 1024), lane i landing at base + 16 i, with no
-// VGPR round trip; completion is tracked by vmcnt. wait_async() + a barrier publishes the data.
+// Asynchronous global -> LDS staging with buffer_load_dwordx4 ... lds (MUBUF): one wave
+// instruction copies 64 x 16 bytes into LDS bytes [M0, M0 + 1024), lane i landing at
+// M0 + 16 i, with no VGPR round trip; completion is tracked by vmcnt, and wait_async() plus a
+// barrier publishes the data. (The FLAT-encoded global_load_lds would do the same copy, but
+// while a FLAT instruction that may touch LDS is in flight the compiler's wait insertion
+// cannot tell it from an LDS read and flushes lgkmcnt to zero before every LDS operand use,
+// which serialises read-ahead fragment loads.)
 //
-// Stage `rows` rows of D 16-bit elements starting at global row `grow0` of a head into a
-// swizzled tile. Rows at or past `n_rows` read row n_rows - 1 instead (finite data that the
-// kernels mask), so no load leaves the tensor. Waves `wave`, `wave + nw`, ... split the work.
-template <int D, int ROWS, int NW>
-__device__ __forceinline__ void stage_rows_swz(uint16_t* tile, const uint16_t* head, int grow0, int n_rows,
-                                               int wave) {
-  constexpr int ROW_BYTES = D * 2;
-  constexpr int N_INST = ROWS * ROW_BYTES / 1024;
-  // Every wave issues the same, compile-time number of copies, so the compiler's vmcnt
-  // bookkeeping is exact (it then waits only for the copies a read actually depends on).
-  static_assert(N_INST % NW == 0, "tile copies must split evenly over the waves");
-  const int l = lane_id();
-#pragma unroll
-  for (int k = 0; k < N_INST / NW; ++k) {
-    const int ins = wave + k * NW;
-    const int p = ins * 1024 + l * 16;
-    const int row = p / ROW_BYTES;
-    const int lchunk = ((p % ROW_BYTES) >> 4) ^ swz<D>(row);
-    const int grow = min(grow0 + row, n_rows - 1);
-    __builtin_amdgcn_global_load_lds(head + (size_t)grow * D + lchunk * 8, tile + ins * 512, 16, 0, 0);
-  }
-}
-
-// The same copy through buffer_load_dwordx4 ... lds (MUBUF) instead of the FLAT-encoded
-// global_load_lds. While a FLAT instruction that may touch LDS is in flight, the compiler's
-// wait insertion cannot tell its LDS side from ordinary LDS reads and waits for lgkmcnt(0)
-// before every LDS operand use, which serialises read-ahead LDS fragment loads; the MUBUF copy
-// is counted on vmcnt only. The descriptor covers just the rows that exist: rows at or past
-// `n_rows` read as zero (hardware range check), finite data that the kernels mask.
-// Word 3 of the descriptor (0x00020000) is the gfx9 setting for untyped 32-bit access.
+// A descriptor covers just the rows that exist: reads at or past its size return zero (the
+// hardware range check), finite data that the kernels mask, and no load leaves the tensor.
+// Word 3 (0x00020000) is the gfx9 setting for untyped 32-bit access. Base and size are
+// wave-uniform by contract; readfirstlane pins them to SGPRs (a descriptor the compiler sees
+// in VGPRs turns each copy into a per-lane loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 // Descriptor of the rows [grow0, grow0 + ROWS) of a head that exist (n_rows rows in all).
 template <int D, int ROWS>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* head, int grow0, int n_rows) {
-  // (readfirstlane: the value is wave-uniform; keeping it in an SGPR keeps the descriptor
-  // scalar, which the buffer instruction requires)
   const int avail = __builtin_amdgcn_readfirstlane(max(0, min(n_rows - grow0, ROWS)));
   return make_rsrc(head + (size_t)grow0 * D, avail * D * 2);
 }
-// Copy k (0 <= k < ROWS*D*2/1024/NW) of wave `wave`'s share of a ROWS-row tile: 1 KB, i.e.
-// 1024/(2D) whole rows, landing swizzled at tile[ins * 512 ...], ins = wave + k*NW.
+// Copy k (0 <= k < ROWS*D*2/1024/NW) of wave `wave`'s share of a ROWS-row tile of D 16-bit
+// elements: 1 KB, i.e. 1024/(2D) whole rows, landing swizzled at tile[ins * 512 ...],
+// ins = wave + k*NW. Every wave issues the same, compile-time number of copies, so the
+// compiler's vmcnt bookkeeping is exact.
 template <int D, int ROWS, int NW>
 __device__ __forceinline__ void stage_copy(uint16_t* tile, __amdgpu_buffer_rsrc_t rsrc, int wave, int k) {
   constexpr int ROW_BYTES = D * 2;
@@ -309,6 +292,7 @@ __device__ __forceinline__ void stage_copy(uint16_t* tile, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)(tile + ins * 512), 16, row * ROW_BYTES + lchunk * 16, 0,
                                            0, 0);
 }
+// All of wave `wave`'s copies of the tile at rows [grow0, grow0 + ROWS).
 template <int D, int ROWS, int NW>
 __device__ __forceinline__ void stage_rows_swz_buf(uint16_t* tile, const uint16_t* head, int grow0, int n_rows,
                                                    int wave) {
@@ -317,12 +301,17 @@ __device__ __forceinline__ void stage_rows_swz_buf(uint16_t* tile, const uint16_
   for (int k = 0; k < ROWS * D * 2 / 1024 / NW; ++k) stage_copy<D, ROWS, NW>(tile, rsrc, wave, k);
 }
 
-// Stage 64 floats: lanes 0..31 from a[r0 + i], lanes 32..63 from b[r0 + i - 32] (rows clamped
-// to n_rows - 1), into dst[0..63] (one wave instruction).
-__device__ __forceinline__ void stage_stats(float* dst, const float* a, const float* b, int r0, int n_rows) {
-  const int l = lane_id();
-  const int r = min(r0 + (l & 31), n_rows - 1);
-  __builtin_amdgcn_global_load_lds((l < 32 ? a : b) + r, dst, 4, 0, 0);
+// Per-row statistics of 32 rows from two arrays: dst[0..31] = a[r0 ..], dst[64..95] =
+// b[r0 ..] (dst holds 128 floats; [32..63] and [96..127] receive copies of the same values).
+// Two full-wave copies with one descriptor each: lane-divergent copies from two descriptors
+// get merged by the compiler into one copy with a per-lane descriptor.
+constexpr int kStatB = 64;  // offset of the second array's values in a statistics slot
+__device__ __forceinline__ void stage_stats_buf(float* dst, const float* a, const float* b, int r0, int n_rows) {
+  const int voff = (lane_id() & 31) * 4;
+  const int avail = max(0, min(n_rows - r0, 32));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a + r0, avail * 4), (FA_LDS void*)dst, 4, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b + r0, avail * 4), (FA_LDS void*)(dst + kStatB), 4, voff, 0, 0,
+                                           0);
 }
 
 // vmcnt(0) through the builtin rather than inline asm, so the compiler's wait-insertion pass

@@ -65,8 +65,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   // A head's Q tiles run together on one XCD (shared K/V reads in its L2), heaviest
   // causal tile first.
   const int lid = xcd_local_index(blockIdx.x, BH * n_qtiles);
-  const int bh = lid / n_qtiles;
-  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
+  const int bh = __builtin_amdgcn_readfirstlane(lid / n_qtiles);  // wave-uniform (keeps pointers scalar)
+  const int qt = __builtin_amdgcn_readfirstlane(CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles));
   const int q0 = qt * BM;
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row
 
