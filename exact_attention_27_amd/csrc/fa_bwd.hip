@@ -46,23 +46,32 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
 }
 
 // ------------------------------------------------------------------------------------------
-// [3] dQ. Workgroup = NW waves, each owning QB*32 query rows (Q, dO, LSE, D pinned); K/V
-// tiles of BN keys are copied global -> LDS (swizzled) by the asynchronous loads into a
+// [3] dQ. Workgroup = NW waves, each owning 32 query rows (Q, dO, LSE, D pinned); K/V tiles of
+// BN = 32 keys are copied global -> LDS (swizzled) by the asynchronous loads into a
 // double-buffered ring.
-template <typename T, int D, int BN, int NW, int QB, int NBUF, bool CAUSAL>
+//
+// Per step and wave, S^T = K Q^T and dP^T = V dO^T put one query row in each lane (its LSE
+// and D are per-lane scalars). The step is written as three sched_barrier-fenced phases of
+// 8 MFMAs with the LDS fragment reads issued ahead of their MFMA:
+//   [S]  S^T = K Q^T          || the copies of the next K / V tile
+//   [dP] dP^T = V dO^T        || P = 2^(c S - LSE log2 e)
+//   [dQ] dQ^T += K^T dS^T     || dS = P (dP - D) of the second 16-key group
+// Steps on the causal diagonal or the key tail run a copy of the body with the mask.
+template <typename T, int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, int BH, int N, int n_qtiles, float scale, float c_log2) {
-  constexpr int BM = NW * QB * 32;
+  constexpr int BN = 32;
+  constexpr int BM = NW * 32;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int KB = BN / 32;
+  constexpr int CPW = BN * D * 2 / 1024 / NW;  // tile copies per wave per K (or V) tile
+  static_assert(CPW >= 1, "each wave copies at least one KB of a tile");
 
   // K is read by rows (S^T) and transposed (dQ), V by rows: swizzled layout for both.
   // One array per ring slot: with every slot index a compile-time constant the compiler can
   // tell a copy into one slot from reads of another and does not wait for the copy first.
-  static_assert(NBUF == 2, "ring of two slots");
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[BN * D];
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   const int bh = __builtin_amdgcn_readfirstlane(lid / n_qtiles);  // wave-uniform (keeps pointers scalar)
   const int qt = __builtin_amdgcn_readfirstlane(CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles));
   const int q0 = qt * BM;
-  const int qw0 = q0 + wave * QB * 32;
+  const int qrow = q0 + wave * 32 + l32;  // this lane's query row
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* Kh = K + head;
@@ -88,133 +97,177 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
-  auto stage = [&](int t, uint16_t* kdst, uint16_t* vdst) {
-    stage_rows_swz_buf<D, BN, NW>(kdst, Kh, t * BN, N, wave);
-    stage_rows_swz_buf<D, BN, NW>(vdst, Vh, t * BN, N, wave);
-  };
-  stage(0, lds_k0, lds_v0);
+  // Tiles [0, n_plain) have every key visible to every row of the workgroup: no mask.
+  const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
 
-  Frag qf[QB][KS], dof[QB][KS];
-  float lse2[QB], dl[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qw0 + qb * 32 + l32;
+  stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, N, wave);
+  stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, N, wave);
+
+  Frag qf[KS], dof[KS];
+  float lse2, dl;
+  {
     const bool ok = qrow < N;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[qb][ks].v = gload16(Q + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
-      dof[qb][ks].v = gload16(dO + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
+      qf[ks].v = gload16(Q + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
+      dof[ks].v = gload16(dO + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
     }
-    lse2[qb] = ok ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
-    dl[qb] = ok ? Delta[(size_t)bh * N + qrow] : 0.f;
+    lse2 = ok ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+    dl = ok ? Delta[(size_t)bh * N + qrow] : 0.f;
   }
 
-  f32x16 acc[QB][DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  // Per-lane fragment base offsets (every fragment address is one XOR / add away).
-  const int rows0 = swz_rows_base<D>(0);
-  const int cols0 = swz_cols_base<D>();
+  // Loop-invariant per-lane byte offsets of every fragment read (the swizzle is linear over
+  // XOR): K / V row reads need one offset per k-step, K^T transposing reads two per 32-column
+  // block; row steps are adds folded into the instructions.
+  int rofs[KS], cofs[DB][2];
+  {
+    const int r0 = swz_rows_base<D>(0) * 2, c0 = swz_cols_base<D>() * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rofs[ks] = r0 ^ (ks << 5);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      cofs[db][0] = c0 ^ (db << 6);
+      cofs[db][1] = cofs[db][0] ^ 32;
+    }
+  }
+  auto tfrag = [&](const uint16_t* tile, int db, int krow0) __attribute__((always_inline)) {
+    return lds_read_cols(tile, cofs[db][0] + krow0 * D * 2, cofs[db][1] + (krow0 + 8) * D * 2);
+  };
 
   wait_async();
   __syncthreads();
 
-  // One K/V tile per call; `ks_base`/`vs_base` hold tile t, the other slot receives tile
-  // t+1 (clamped: the prefetch is unconditional).
-  auto tile_step = [&](int t, const uint16_t* ks_base, const uint16_t* vs_base, uint16_t* knext,
-                       uint16_t* vnext) {
-    stage(min(t + 1, ntiles - 1), knext, vnext);
+  // One K/V tile: reads slots (kc, vc) holding tile t, copies tile t+1 (clamped: the
+  // prefetch is unconditional) into (kn, vn). Register i of S^T / dP^T holds key
+  // t*BN + 8(i/4) + 4h + (i%4) of this lane's query row.
+  auto step = [&](auto mask_tag, int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn)
+                  __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int kbase = t * BN;
-    // Every wave runs every K/V tile of the workgroup's range (fully masked tiles add 0;
-    // that includes the padding step when the tile count is odd).
-    const bool need_mask = (kbase + BN > N) || (CAUSAL && (kbase + BN - 1 > qw0));
-    f32x16 s[QB][KB], dp[QB][KB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[qb][kb][i] = 0.f;
-          dp[qb][kb][i] = 0.f;
-        }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    const int tn = min(t + 1, ntiles - 1);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, tn * BN, N);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, BN>(Vh, tn * BN, N);
+
+    // ---- [S]: chunk ks issues a tile copy every GAP chunks, the K fragment read for MFMA
+    // ks+2 and MFMA ks.
+    f32x16 s, dp;
+    {
+      constexpr int GAP = KS / (2 * CPW);
+      static_assert(GAP >= 1 && KS % (2 * CPW) == 0, "copies must spread evenly over [S]");
+      Frag fr[3];
+      fr[0] = lds_read_rows(kc, rofs[0]);
+      fr[1] = lds_read_rows(kc, rofs[1]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Frag ak = swz_rows_frag<D>(ks_base, rows0 + kb * 32 * D, ks);
-        const Frag av = swz_rows_frag<D>(vs_base, rows0 + kb * 32 * D, ks);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          s[qb][kb] = T::mfma(ak, qf[qb][ks], s[qb][kb]);
-          dp[qb][kb] = T::mfma(av, dof[qb][ks], dp[qb][kb]);
+        if (ks % GAP == 0) {
+          const int c = ks / GAP;
+          if (c < CPW)
+            stage_copy<D, BN, NW>(kn, rk, wave, c);
+          else
+            stage_copy<D, BN, NW>(vn, rv, wave, c - CPW);
         }
-      }
-    Frag dsf[QB][KB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = qw0 + qb * 32 + l32;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = __builtin_fmaf(s[qb][kb][i], c_log2, -lse2[qb]);
-          // hidden entries get 2^-inf = 0 (a select on the exponent input, no branch)
-          const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          // (bitwise, not short-circuit, operators: keeps this a select instead of branches)
-          const bool hidden = need_mask & ((key >= N) | (CAUSAL & (key > qrow)));
-          x = hidden ? -INFINITY : x;
-          const float p = __builtin_amdgcn_exp2f(x);
-          dp[qb][kb][i] = p * (dp[qb][kb][i] - dl[qb]);
-        }
-        dsf[qb][kb][0] = pack_group<T>(dp[qb][kb], 0);
-        dsf[qb][kb][1] = pack_group<T>(dp[qb][kb], 1);
+        if (ks + 2 < KS) fr[(ks + 2) % 3] = lds_read_rows(kc, rofs[ks + 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        s = T::mfma(fr[ks % 3], qf[ks], ks == 0 ? f32x16{} : s);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+
+    // ---- [dP]: chunk ks issues the V fragment read for MFMA ks+2, MFMA ks and 16/KS
+    // exponentials of S.
+    {
+      constexpr int EPC = 16 / KS;
+      Frag fr[3];
+      fr[0] = lds_read_rows(vc, rofs[0]);
+      fr[1] = lds_read_rows(vc, rofs[1]);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 2 < KS) fr[(ks + 2) % 3] = lds_read_rows(vc, rofs[ks + 2]);
+        __builtin_amdgcn_sched_barrier(0);
+        dp = T::mfma(fr[ks % 3], dof[ks], ks == 0 ? f32x16{} : dp);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const Frag a = swz_cols_frag<D>(ks_base, cols0, kb * 32 + tt * 16, db * 32);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = T::mfma(a, dsf[qb][kb][tt], acc[qb][db]);
+        for (int e = 0; e < EPC; ++e) {
+          const int i = ks * EPC + e;
+          float x = __builtin_fmaf(s[i], c_log2, -lse2);
+          if (MASK) {
+            // hidden entries get 2^-inf = 0 (a select on the exponent input; bitwise
+            // operators keep it a select instead of branches)
+            const int key = kbase + 8 * (i / 4) + 4 * h + (i % 4);
+            const bool hidden = (key >= N) | (CAUSAL & (key > qrow));
+            x = hidden ? -INFINITY : x;
+          }
+          s[i] = __builtin_amdgcn_exp2f(x);
         }
-    // Tile t+1 must have landed: allow the NBUF-2 younger tiles to stay in flight.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- dS = P (dP - D) of the first 16-key group, then [dQ]: chunk j (group tt = j / DB,
+    // d block db = j % DB) issues the K^T fragment read for MFMA j+1, MFMA j, and during the
+    // first group's MFMAs dS of the second group.
+    {
+      constexpr int NJ = 2 * DB;
+      constexpr int EPC = 8 / DB;  // second-group elements per first-group chunk
+      Frag dsf[2];
+      Frag fr[2];
+      fr[0] = tfrag(kc, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dp[i] = s[i] * (dp[i] - dl);
+      dsf[0] = pack_group<T>(dp, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j + 1 < NJ) fr[(j + 1) % 2] = tfrag(kc, (j + 1) % DB, ((j + 1) / DB) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[j % DB] = T::mfma(fr[j % 2], dsf[j / DB], acc[j % DB]);
+        if (j < DB) {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            const int i = 8 + j * EPC + e;
+            dp[i] = s[i] * (dp[i] - dl);
+            if (i % 2 == 1) dsf[1].v[(i - 8) / 2] = T::pack2(dp[i - 1], dp[i]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
     // Tile t+1 must have landed before anyone reads it.
     wait_async();
     ring_barrier();
   };
-  // Two steps per trip with the slots fixed at compile time; an odd tile count gets one
-  // fully masked padding step (its keys are past the causal range or past N).
-  for (int t = 0; t < ntiles; t += 2) {
-    tile_step(t, lds_k0, lds_v0, lds_k1, lds_v1);
-    tile_step(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
-  }
+
+  // Two steps per trip with the slots fixed at compile time; the masked loop takes the
+  // causal diagonal and the key tail, with one fully masked padding step (its keys are past
+  // the causal range or past N) when the count is odd.
+  using F = std::false_type;
+  using Tr = std::true_type;
+  auto pair = [&](auto mask_tag, int t) __attribute__((always_inline)) {
+    step(mask_tag, t, lds_k0, lds_v0, lds_k1, lds_v1);
+    step(mask_tag, t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+  };
+  int t = 0;
+  for (; t + 2 <= n_plain; t += 2) pair(F(), t);
+  for (; t < ntiles; t += 2) pair(Tr(), t);
   // No copy may still be landing in LDS when the workgroup retires.
   wait_async();
 
+  if (qrow < N) {
+    uint16_t* row = dQ + head + (size_t)qrow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qw0 + qb * 32 + l32;
-    if (qrow < N) {
-      uint16_t* row = dQ + head + (size_t)qrow * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w;
-          w[0] = T::pack2(acc[qb][db][4 * g + 0] * scale, acc[qb][db][4 * g + 1] * scale);
-          w[1] = T::pack2(acc[qb][db][4 * g + 2] * scale, acc[qb][db][4 * g + 3] * scale);
-          *reinterpret_cast<u32x2*>(row + db * 32 + 8 * g + 4 * h) = w;
-        }
-    }
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = T::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale);
+        w[1] = T::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
+        *reinterpret_cast<u32x2*>(row + db * 32 + 8 * g + 4 * h) = w;
+      }
   }
 }
 
@@ -234,11 +287,11 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a) {
-  constexpr int NW = 4, QB = 1, BN = 32, NBUF = 2;
-  constexpr int BM = NW * QB * 32;
+  constexpr int NW = 4;
+  constexpr int BM = NW * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
   const long long grid = (long long)n_qtiles * a.BH;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW, QB, NBUF, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dq, a.BH, a.N, n_qtiles, a.scale,
                      a.c_log2);
