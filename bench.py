@@ -31,7 +31,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_common.hpp"],
     "bwd_preprocess": ["fa_bwd.hip", "fa_common.hpp"],
-    "bwd_dkv": ["fa_bwd.hip", "fa_common.hpp"],
+    "bwd_dkv": ["fa_bwd_dkv.hip", "fa_common.hpp"],
     "bwd_dq": ["fa_bwd.hip", "fa_common.hpp"],
 }
 
@@ -97,7 +97,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llm_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--cpu-heads", type=int, default=128)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling HBM byte counters)")
