@@ -47,22 +47,22 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
 
 // ------------------------------------------------------------------------------------------
 // [3] dQ. Workgroup = NW waves, each owning 32 query rows (Q, dO, LSE, D pinned); K/V tiles of
-// BN = 32 keys are copied global -> LDS (swizzled) by the asynchronous loads into a
+// BN keys are copied global -> LDS (swizzled) by the asynchronous loads into a
 // double-buffered ring.
 //
 // Per step and wave, S^T = K Q^T and dP^T = V dO^T put one query row in each lane (its LSE
 // and D are per-lane scalars). The step is written as three sched_barrier-fenced phases of
-// 8 MFMAs with the LDS fragment reads issued ahead of their MFMA:
+// BN/32 * 8 MFMAs with the LDS fragment reads issued ahead of their MFMA:
 //   [S]  S^T = K Q^T          || the copies of the next K / V tile
 //   [dP] dP^T = V dO^T        || P = 2^(c S - LSE log2 e)
-//   [dQ] dQ^T += K^T dS^T     || dS = P (dP - D) of the second 16-key group
+//   [dQ] dQ^T += K^T dS^T     || dS = P (dP - D) of the next 16-key group
 // Steps on the causal diagonal or the key tail run a copy of the body with the mask.
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int BN, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, int BH, int N, int n_qtiles, float scale, float c_log2) {
-  constexpr int BN = 32;
+  constexpr int KB = BN / 32;  // 32-key blocks per K/V tile
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -149,88 +149,99 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   auto step = [&](auto mask_tag, int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn)
                   __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int NA = KB * KS;  // MFMAs of the [S] and of the [dP] phase
     const int kbase = t * BN;
     const int tn = min(t + 1, ntiles - 1);
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, tn * BN, N);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, BN>(Vh, tn * BN, N);
+    // fragment i of a K or V tile: key block i % KB (so consecutive MFMAs are independent),
+    // k-step i / KB
+    auto rfrag = [&](const uint16_t* tile, int i) {
+      return lds_read_rows(tile, rofs[i / KB] + (i % KB) * 32 * D * 2);
+    };
 
-    // ---- [S]: chunk ks issues a tile copy every GAP chunks, the K fragment read for MFMA
-    // ks+2 and MFMA ks.
-    f32x16 s, dp;
+    // ---- [S]: chunk i issues a tile copy every GAP chunks, the K fragment read for MFMA i+2
+    // and MFMA i.
+    f32x16 s[KB], dp[KB];
     {
-      constexpr int GAP = KS / (2 * CPW);
-      static_assert(GAP >= 1 && KS % (2 * CPW) == 0, "copies must spread evenly over [S]");
+      constexpr int GAP = NA / (2 * CPW);
+      static_assert(GAP >= 1 && NA % (2 * CPW) == 0, "copies must spread evenly over [S]");
       Frag fr[3];
-      fr[0] = lds_read_rows(kc, rofs[0]);
-      fr[1] = lds_read_rows(kc, rofs[1]);
+      fr[0] = rfrag(kc, 0);
+      fr[1] = rfrag(kc, 1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks % GAP == 0) {
-          const int c = ks / GAP;
+      for (int i = 0; i < NA; ++i) {
+        if (i % GAP == 0) {
+          const int c = i / GAP;
           if (c < CPW)
             stage_copy<D, BN, NW>(kn, rk, wave, c);
           else
             stage_copy<D, BN, NW>(vn, rv, wave, c - CPW);
         }
-        if (ks + 2 < KS) fr[(ks + 2) % 3] = lds_read_rows(kc, rofs[ks + 2]);
+        if (i + 2 < NA) fr[(i + 2) % 3] = rfrag(kc, i + 2);
         __builtin_amdgcn_sched_barrier(0);
-        s = T::mfma(fr[ks % 3], qf[ks], ks == 0 ? f32x16{} : s);
+        const int kb = i % KB, ks = i / KB;
+        s[kb] = T::mfma(fr[i % 3], qf[ks], ks == 0 ? f32x16{} : s[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // ---- [dP]: chunk ks issues the V fragment read for MFMA ks+2, MFMA ks and 16/KS
+    // ---- [dP]: chunk i issues the V fragment read for MFMA i+2, MFMA i and 16/KS
     // exponentials of S.
     {
-      constexpr int EPC = 16 / KS;
+      constexpr int EPC = 16 * KB / NA;
       Frag fr[3];
-      fr[0] = lds_read_rows(vc, rofs[0]);
-      fr[1] = lds_read_rows(vc, rofs[1]);
+      fr[0] = rfrag(vc, 0);
+      fr[1] = rfrag(vc, 1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 2 < KS) fr[(ks + 2) % 3] = lds_read_rows(vc, rofs[ks + 2]);
+      for (int i = 0; i < NA; ++i) {
+        if (i + 2 < NA) fr[(i + 2) % 3] = rfrag(vc, i + 2);
         __builtin_amdgcn_sched_barrier(0);
-        dp = T::mfma(fr[ks % 3], dof[ks], ks == 0 ? f32x16{} : dp);
+        const int kb = i % KB, ks = i / KB;
+        dp[kb] = T::mfma(fr[i % 3], dof[ks], ks == 0 ? f32x16{} : dp[kb]);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-          const int i = ks * EPC + e;
-          float x = __builtin_fmaf(s[i], c_log2, -lse2);
+          const int idx = i * EPC + e, b = idx / 16, r = idx % 16;
+          float x = __builtin_fmaf(s[b][r], c_log2, -lse2);
           if (MASK) {
             // hidden entries get 2^-inf = 0 (a select on the exponent input; bitwise
             // operators keep it a select instead of branches)
-            const int key = kbase + 8 * (i / 4) + 4 * h + (i % 4);
+            const int key = kbase + b * 32 + 8 * (r / 4) + 4 * h + (r % 4);
             const bool hidden = (key >= N) | (CAUSAL & (key > qrow));
             x = hidden ? -INFINITY : x;
           }
-          s[i] = __builtin_amdgcn_exp2f(x);
+          s[b][r] = __builtin_amdgcn_exp2f(x);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // ---- dS = P (dP - D) of the first 16-key group, then [dQ]: chunk j (group tt = j / DB,
-    // d block db = j % DB) issues the K^T fragment read for MFMA j+1, MFMA j, and during the
-    // first group's MFMAs dS of the second group.
+    // ---- dS = P (dP - D) of the first 16-key group, then [dQ]: chunk j (group g = j / DB,
+    // keys 16g .. 16g+15 of the tile, d block db = j % DB) issues the K^T fragment read for
+    // MFMA j+1, MFMA j, and during group g's MFMAs dS of group g+1.
     {
-      constexpr int NJ = 2 * DB;
-      constexpr int EPC = 8 / DB;  // second-group elements per first-group chunk
-      Frag dsf[2];
+      constexpr int NG = 2 * KB;   // 16-key groups
+      constexpr int NJ = NG * DB;
+      constexpr int EPC = 8 / DB;  // next-group elements per chunk
+      Frag dsf[NG];
       Frag fr[2];
       fr[0] = tfrag(kc, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dp[i] = s[i] * (dp[i] - dl);
-      dsf[0] = pack_group<T>(dp, 0);
+      for (int r = 0; r < 8; ++r) dp[0][r] = s[0][r] * (dp[0][r] - dl);
+      dsf[0] = pack_group<T>(dp[0], 0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
+        const int g = j / DB, db = j % DB;
         if (j + 1 < NJ) fr[(j + 1) % 2] = tfrag(kc, (j + 1) % DB, ((j + 1) / DB) * 16);
         __builtin_amdgcn_sched_barrier(0);
-        acc[j % DB] = T::mfma(fr[j % 2], dsf[j / DB], acc[j % DB]);
-        if (j < DB) {
+        acc[db] = T::mfma(fr[j % 2], dsf[g], acc[db]);
+        if (g + 1 < NG) {
+          const int gn = g + 1, b = gn / 2;
 #pragma unroll
           for (int e = 0; e < EPC; ++e) {
-            const int i = 8 + j * EPC + e;
-            dp[i] = s[i] * (dp[i] - dl);
-            if (i % 2 == 1) dsf[1].v[(i - 8) / 2] = T::pack2(dp[i - 1], dp[i]);
+            const int r = 8 * (gn % 2) + db * EPC + e;
+            dp[b][r] = s[b][r] * (dp[b][r] - dl);
+            if (r % 2 == 1) dsf[gn].v[(r % 8) / 2] = T::pack2(dp[b][r - 1], dp[b][r]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -287,11 +298,11 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a) {
-  constexpr int NW = 4;
+  constexpr int NW = 4, BN = 64;
   constexpr int BM = NW * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
   const long long grid = (long long)n_qtiles * a.BH;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dq, a.BH, a.N, n_qtiles, a.scale,
                      a.c_log2);
