@@ -59,12 +59,20 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // A head's K tiles run together on one XCD (shared Q/dO reads in its L2); causal: low
-  // key tiles see the most queries and go first.
+  // Causal: low key tiles see the most queries; a workgroup takes the pair of key tiles
+  // (p, n_ktiles-1-p), the heavy one first, so every workgroup streams the same number of Q
+  // tiles; an odd middle tile runs alone. A head's workgroups run together on one XCD (shared
+  // Q/dO reads in its L2).
   const int n_ktiles = (N + BK - 1) / BK;
-  const int lid = xcd_local_index(blockIdx.x, BH * n_ktiles);
-  const int bh = __builtin_amdgcn_readfirstlane(lid / n_ktiles);  // wave-uniform (keeps
-  const int kt = __builtin_amdgcn_readfirstlane(lid % n_ktiles);  // pointers scalar)
+  const int npairs = CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles;
+  const int lid = xcd_local_index(blockIdx.x, BH * npairs);
+  const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
+  const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
+  const int npass = (CAUSAL && n_ktiles - 1 - pr != pr) ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+  const int kt = pass == 0 ? pr : n_ktiles - 1 - pr;
+  // every wave is done with the previous tile's LDS slots before this tile's copies start
+  if (pass > 0) __syncthreads();
   const int k0 = kt * BK;
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
@@ -282,6 +290,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
         *reinterpret_cast<u32x2*>(dv_row + db * 32 + 8 * g + 4 * h) = wv;
       }
   }
+  }  // pass
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -289,7 +298,7 @@ static hipError_t launch_dkv_t(const BwdArgs& a) {
   constexpr int NW = 4;
   constexpr int BK = NW * 32;
   const int n_ktiles = (a.N + BK - 1) / BK;
-  const long long grid = (long long)n_ktiles * a.BH;
+  const long long grid = (long long)(CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles) * a.BH;
   hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.BH, a.N, a.scale,

@@ -62,11 +62,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // A head's Q tiles run together on one XCD (shared K/V reads in its L2), heaviest
-  // causal tile first.
-  const int lid = xcd_local_index(blockIdx.x, BH * n_qtiles);
-  const int bh = __builtin_amdgcn_readfirstlane(lid / n_qtiles);  // wave-uniform (keeps pointers scalar)
-  const int qt = __builtin_amdgcn_readfirstlane(CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles));
+  // Causal: a workgroup takes the pair of Q tiles (n_qtiles-1-p, p), the heavy one first, so
+  // every workgroup has the same number of K/V tiles (no tail of long-running workgroups at the
+  // end of the grid); an odd middle tile runs alone. A head's workgroups run together on one
+  // XCD (shared K/V reads in its L2).
+  const int npairs = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int lid = xcd_local_index(blockIdx.x, BH * npairs);
+  const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
+  const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
+  const int npass = (CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+  const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - pr : pr) : pr;
+  // every wave is done with the previous tile's LDS slots before this tile's copies start
+  if (pass > 0) __syncthreads();
   const int q0 = qt * BM;
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row
 
@@ -382,6 +390,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
       }
     if (LSE != nullptr && h == 0) LSE[(size_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
   }
+  }  // pass
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -389,7 +398,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int NW = 4, BN = 64;
   constexpr int BM = NW * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
-  const long long grid = (long long)n_qtiles * a.BH;
+  const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * a.BH;
   hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.BH, a.N, n_qtiles, a.c_log2);
