@@ -106,6 +106,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   const int ntiles = (kv_end + BN - 1) / BN;
   // Tiles [0, n_plain) have every key visible to every row of the workgroup: no mask.
   const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
+  // Keys past N, and with the causal mask keys after the row, are hidden: key <= key_lim.
+  const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 
   stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, N, wave);
   stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, N, wave);
@@ -157,7 +159,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
                   __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int NA = KB * KS;  // MFMAs of the [S] and of the [dP] phase
-    const int kbase = t * BN;
+    // Register r of key block b holds key t*BN + 4h + b*32 + 8(r/4) + (r%4); it is visible to
+    // this lane's row iff key <= key_lim, i.e. iff its compile-time offset is <= thr.
+    const int thr = key_lim - t * BN - 4 * h;
     const int tn = min(t + 1, ntiles - 1);
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, tn * BN, N);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, BN>(Vh, tn * BN, N);
@@ -211,11 +215,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
           const int idx = i * EPC + e, b = idx / 16, r = idx % 16;
           float x = __builtin_fmaf(s[b][r], c_log2, -lse2);
           if (MASK) {
-            // hidden entries get 2^-inf = 0 (a select on the exponent input; bitwise
-            // operators keep it a select instead of branches)
-            const int key = kbase + b * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-            const bool hidden = (key >= N) | (CAUSAL & (key > qrow));
-            x = hidden ? -INFINITY : x;
+            // hidden entries get 2^-inf = 0: a select on the exponent input when the
+            // element's compile-time key offset exceeds the lane's threshold
+            x = (b * 32 + 8 * (r / 4) + (r % 4)) > thr ? -INFINITY : x;
           }
           s[b][r] = __builtin_amdgcn_exp2f(x);
         }

@@ -136,6 +136,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
                   uint16_t* don, float* stn) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int qbase = it * BQ;
+    // Register i holds query row qbase + 4h + 8(i/4) + (i%4) of this lane's key. It is visible
+    // iff the row is < N, the key is < N and (causal) the row is >= the key, i.e. iff the
+    // compile-time offset 8(i/4) + (i%4) lies in [vis_lo, vis_hi); one unsigned compare.
+    const int vis_lo = CAUSAL ? key - qbase - 4 * h : -(1 << 24);
+    const int vis_hi = key < N ? N - qbase - 4 * h : vis_lo;
+    const uint32_t vis_span = (uint32_t)max(vis_hi - vis_lo, 0);
     // this wave's V rows: base offset re-materialised each step (kept opaque so the compiler
     // adds it per read instead of holding KS more loop-invariant addresses)
     int vrow = wave * 32 * D * 2;
@@ -199,11 +205,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
           const int i = ks * EPC + e;
           float x = __builtin_fmaf(s[i], c_log2, -st4[i / 4][i % 4] * kLog2e);
           if (MASK) {
-            // hidden entries get 2^-inf = 0 (a select on the exponent input, no branch;
-            // bitwise operators keep it a select)
-            const int qrow = qbase + 8 * (i / 4) + 4 * h + (i % 4);
-            const bool hidden = (qrow >= N) | (key >= N) | (CAUSAL & (key > qrow));
-            x = hidden ? -INFINITY : x;
+            // hidden entries get 2^-inf = 0: a select on the exponent input unless the
+            // element's compile-time row offset lies in [vis_lo, vis_lo + vis_span)
+            x = (uint32_t)(8 * (i / 4) + (i % 4) - vis_lo) >= vis_span ? -INFINITY : x;
           }
           s[i] = __builtin_amdgcn_exp2f(x);
           if (i % 2 == 1) pf[i / 8].v[(i % 8) / 2] = T::pack2(s[i - 1], s[i]);

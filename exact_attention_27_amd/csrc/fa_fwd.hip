@@ -146,18 +146,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
       for (int ks = 1; ks < KS; ++ks) s[kb] = T::mfma(kfrag(ktile, kb * KS + ks), qf[ks], s[kb]);
     }
   };
-  // Hide keys past N and (causal) keys after this lane's row.
+  // Masking. A key is visible to this lane's row iff key <= key_lim (keys past N, and with the
+  // causal mask keys after the row, are hidden). Register i of key block kb holds key
+  // kbase + 4h + kb*32 + 8(i/4) + (i%4), so with thr = key_lim - kbase - 4h an element is
+  // hidden iff the compile-time offset kb*32 + 8(i/4) + (i%4) exceeds thr: one compare and one
+  // select per element.
+  const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+  auto mask_thr = [&](int t) { return key_lim - t * BN - 4 * h; };
+  auto masked = [](float x, int kb, int i, int thr) {
+    return (kb * 32 + 8 * (i >> 2) + (i & 3)) > thr ? -INFINITY : x;
+  };
   auto mask = [&](f32x16 (&s)[KB], int t) {
-    const int kbase = t * BN;
+    const int thr = mask_thr(t);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kbase + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        // bitwise, not short-circuit, operators: a select per element instead of branches
-        const bool hidden = (key >= N) | (CAUSAL & (key > qrow));
-        s[kb][i] = hidden ? -INFINITY : s[kb][i];
-      }
+      for (int i = 0; i < 16; ++i) s[kb][i] = masked(s[kb][i], kb, i, thr);
   };
   // Row max of a scores tile -> new reference (moved lazily: only when the tile's max exceeds
   // the reference by more than kTau; otherwise p = 2^(c s - m_ref) <= 2^kTau accumulates
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
       vf[0] = vread(0);
       vf[1] = vread(1);
       float mx = -INFINITY, rs = 0.f;
-      const int kbase = (t + 1) * BN;
+      const int thr = mask_thr(t + 1);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (j + 2 < NB) vf[(j + 2) % 3] = vread(j + 2);
@@ -322,11 +326,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
           rs += s[idx / 16][idx % 16];
           float x = sn[idx / 16][idx % 16];
           if (MASK) {
-            const int i = idx % 16;
-            const int key = kbase + (idx / 16) * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            // bitwise, not short-circuit, operators: a select instead of branches
-            const bool hidden = (key >= N) | (CAUSAL & (key > qrow));
-            x = hidden ? -INFINITY : x;
+            x = masked(x, idx / 16, idx % 16, thr);
             sn[idx / 16][idx % 16] = x;
           }
           mx = fmaxf(mx, x);
