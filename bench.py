@@ -90,6 +90,68 @@ def cpu_baseline(bits, w, heads):
     }
 
 
+def sweep_configs(fa, FI, torch, np, dev, log):
+    """Every workload (and mask setting): forward alone, one fa_backward call, and the split-KV
+    forward with 2 and 4 key ranges, each timed as 11 runs bracketed by HIP events on one
+    stream, the first discarded; counted FLOPs as above."""
+    out = []
+    stream = torch.cuda.current_stream(dev)
+    for key, w in FI.WORKLOADS.items():
+        bits = FI.draw_workload(w)
+        tdt = torch.bfloat16 if w.dtype == FI.BF16 else torch.float16
+        q, k, v, do = (torch.from_numpy(bits[n].view(np.int16)).to(dev).view(tdt) for n in FI.TENSOR_ORDER)
+        o = torch.empty_like(q)
+        lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+        delta = torch.empty_like(lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        for causal in w.causal:
+            F = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if causal else 1.0)
+            res = {}
+            for name, fn in (("fwd", lambda: fa.fa_forward(q, k, v, o, lse, causal, w.scale(), stream)),
+                             ("bwd", lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, causal,
+                                                            w.scale(), stream))):
+                ts = []
+                for _ in range(11):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                ts = np.array(ts[1:]) * 1e3  # us
+                res[name] = {"mean_us": float(ts.mean()), "std_us": float(ts.std()), "median_us": float(np.median(ts))}
+            # the split-KV forward (fa_forward_splitkv) with 2 and 4 key ranges per Q tile
+            for sp in (2, 4):
+                nb = fa.fa_forward_splitkv_workspace_bytes(w.B, w.H, w.N, w.d, sp)
+                if nb > (1 << 30):
+                    continue
+                ws = torch.empty(nb // 4, dtype=torch.float32, device=dev)
+                ts = []
+                for _ in range(11):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fa.fa_forward_splitkv(q, k, v, o, lse, causal, w.scale(), sp, ws, stream)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                ts = np.array(ts[1:]) * 1e3
+                res[f"fwd_split{sp}"] = {"mean_us": float(ts.mean()), "std_us": float(ts.std()),
+                                         "median_us": float(np.median(ts))}
+                del ws
+            fwd_tf = F / (res["fwd"]["mean_us"] * 1e-6) / 1e12
+            tot_tf = 3.5 * F / ((res["fwd"]["mean_us"] + res["bwd"]["mean_us"]) * 1e-6) / 1e12
+            rec = {"workload": key, "label": w.label, "causal": causal, **res,
+                   "fwd_tflops": fwd_tf, "fwd_bwd_tflops": tot_tf}
+            log(f"  {key:13s} causal={int(causal)}  fwd {res['fwd']['mean_us']:9.1f} us (sd {res['fwd']['std_us']:.1f})"
+                f"  bwd {res['bwd']['mean_us']:9.1f} us (sd {res['bwd']['std_us']:.1f})  fwd {fwd_tf:7.1f} TFLOP/s"
+                f"  fwd+bwd {tot_tf:7.1f} TFLOP/s  split-KV fwd: "
+                + ", ".join(f"{k[9:]} ranges {v['mean_us']:.1f} us" for k, v in res.items() if k.startswith("fwd_split")))
+            out.append(rec)
+        del q, k, v, do, o, lse, delta, dq, dk, dv
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +160,8 @@ def main():
     ap.add_argument("--workload", default="llm_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time forward and fa_backward on every workload (table on stderr, 'sweep' in the line)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling HBM byte counters)")
@@ -220,6 +284,11 @@ def main():
         log(f"copy calibration: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
         del src, dst
 
+    sweep = None
+    if args.sweep:
+        log("sweep over the workloads (11 runs each, first discarded):")
+        sweep = sweep_configs(fa, FI, torch, np, dev, log)
+
     cpu = None
     if not args.no_cpu_baseline:
         n = max(1, min(args.cpu_heads, w.B * w.H))
@@ -249,6 +318,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "sweep": sweep,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)

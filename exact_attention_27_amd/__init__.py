@@ -5,7 +5,8 @@ the C ABI declared in include/fa.h. PyTorch supplies device memory and the strea
 There is no CPU or PyTorch fallback: if libfa.so is missing, or a tensor is not on the
 GPU, the call raises.
 
-Raw entry points with the C names (``fa_forward``, ``fa_backward``, ``fa_status_string``)
+Raw entry points with the C names (``fa_forward``, ``fa_forward_splitkv``, ``fa_backward``,
+``fa_status_string``, ...)
 take torch tensors in the documented layouts and return nothing (they raise
 ``FAError`` on a non-zero status). ``attention_forward`` / ``attention_backward`` allocate
 the outputs with torch and call them; ``FlashAttentionFunction`` wraps both for autograd
@@ -27,8 +28,8 @@ FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
-EXPORTED_SYMBOLS = ("fa_forward", "fa_backward", "fa_backward_preprocess", "fa_backward_dkv",
-                    "fa_backward_dq", "fa_status_string")
+EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_splitkv", "fa_forward_splitkv_workspace_bytes", "fa_backward",
+                    "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_status_string")
 
 _lib = None
 
@@ -50,6 +51,10 @@ def load_library() -> ctypes.CDLL:
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_forward.restype = i
+    lib.fa_forward_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+    lib.fa_forward_splitkv.restype = i
+    lib.fa_forward_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_forward_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_backward.restype = i
     lib.fa_backward_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
@@ -114,6 +119,33 @@ def fa_forward(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None
                                    float(scale), _dtype_code(q), _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_forward")
+
+
+def fa_forward_splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int) -> int:
+    return int(load_library().fa_forward_splitkv_workspace_bytes(B, H, N, d, num_splits))
+
+
+def fa_forward_splitkv(q, k, v, o, lse, causal: bool, scale: float, num_splits: int, workspace=None,
+                       stream=None) -> None:
+    """Split-KV forward (same o / lse contract as fa_forward). `workspace` is a float32 GPU tensor
+    of at least fa_forward_splitkv_workspace_bytes(...) bytes; None allocates one with torch."""
+    import torch
+    _check_bhnd("q", q)
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    if lse is not None:
+        _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    need = fa_forward_splitkv_workspace_bytes(B, H, N, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
+    if not workspace.is_cuda or workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 GPU tensor")
+    st = load_library().fa_forward_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                           int(bool(causal)), float(scale), _dtype_code(q), int(num_splits),
+                                           _ptr(workspace), workspace.numel() * 4, _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_splitkv")
 
 
 def fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, causal: bool, scale: float, stream=None) -> None:

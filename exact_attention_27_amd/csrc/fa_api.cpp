@@ -74,8 +74,18 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-               int causal, float scale, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Most key ranges one Q tile may be cut into.
+constexpr int kMaxSplits = 256;
+
+// Bytes of split-KV workspace: per split and row, d fp32 accumulators, a max and a sum.
+long long splitkv_bytes(long long rows, int d, int splits) { return (long long)splits * rows * (d + 2) * 4; }
+
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                 int causal, float scale, int dtype, int splits, float* part, size_t part_bytes, void* stream) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
   if (lse && !aligned16(lse)) return FA_ERR_INVALID_ARG;
@@ -88,6 +98,16 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   if (lse) {
     const Span sl = span(lse, rows * 4);
     if (overlaps(sl, sq) || overlaps(sl, sk) || overlaps(sl, sv) || overlaps(sl, so)) return FA_ERR_INVALID_ARG;
+  }
+  if (splits > 0) {
+    if (!part || !aligned16(part)) return FA_ERR_INVALID_ARG;
+    const long long need = splitkv_bytes(rows, d, splits);
+    if ((unsigned long long)need > (unsigned long long)part_bytes) return FA_ERR_INVALID_ARG;
+    const Span sp = span(part, need);
+    if (overlaps(sp, sq) || overlaps(sp, sk) || overlaps(sp, sv) || overlaps(sp, so)) return FA_ERR_INVALID_ARG;
+    if (lse && overlaps(sp, span(lse, rows * 4))) return FA_ERR_INVALID_ARG;
+    // grid = (N / 128 Q tiles) * splits * B*H workgroups in one 32-bit grid dimension
+    if (((long long)N + 127) / 128 * splits * ((long long)B * H) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   }
   fa::FwdArgs a;
   a.q = q;
@@ -102,7 +122,33 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   a.bf16 = dtype == FA_BF16;
   a.c_log2 = (float)((double)scale * kLog2eD);
   a.stream = stream;
+  a.splits = splits;
+  a.part = part;
   return fa::launch_forward(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               int causal, float scale, int dtype, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, 0, nullptr, 0, stream);
+}
+
+size_t fa_forward_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
+  long long elems = 0, rows = 0;
+  if (check_common(B, H, N, d, 0, 1.0f, FA_BF16, &elems, &rows) != FA_OK) return 0;
+  return (size_t)splitkv_bytes(rows, d, num_splits);
+}
+
+int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                       int d, int causal, float scale, int dtype, int num_splits, float* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, num_splits, workspace, workspace_bytes,
+                      stream);
 }
 
 // Shared validation of backward arguments. Null entries are arguments a stage does not use.

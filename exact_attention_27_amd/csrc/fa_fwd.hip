@@ -39,10 +39,18 @@ namespace fa {
 // Largest tolerated excess of a tile's max over the reference max, in log2 units: p <= 2^8.
 constexpr float kTau = 8.0f;
 
-template <typename T, int D, int BN, int NW, bool CAUSAL>
+// SPLIT: the split-KV form ("FlashAttentionを1から", section "その後の版と、推論での事情":
+// partial softmax states over disjoint key ranges merge exactly). The key tiles of
+// each Q tile are cut into `splits` contiguous ranges, one workgroup each; instead of O and
+// LSE a workgroup writes its unnormalised fp32 accumulator, its reference max (log2 units,
+// -inf for a row that saw no key) and its row sum to `part`, laid out as
+// [splits][BH*N][D] accumulators, then [splits][BH*N] maxima, then [splits][BH*N] sums;
+// merge_kernel combines them.
+template <typename T, int D, int BN, int NW, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, int n_qtiles, float c_log2) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, int n_qtiles, float c_log2,
+    float* __restrict__ part, int splits) {
   constexpr int BM = NW * 32;  // query rows per workgroup
   constexpr int KS = D / 16;   // k-steps over the head dim
   constexpr int DB = D / 32;   // 32-wide blocks of the head dim
@@ -66,13 +74,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   // every workgroup has the same number of K/V tiles (no tail of long-running workgroups at the
   // end of the grid); an odd middle tile runs alone. A head's workgroups run together on one
   // XCD (shared K/V reads in its L2).
-  const int npairs = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  // Split-KV: one workgroup per (head, Q tile, key range), no pairing.
+  const int npairs = SPLIT ? n_qtiles * splits : (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
-  const int npass = (CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
+  const int sp = SPLIT ? pr % splits : 0;  // key range of this workgroup
+  const int npass = (!SPLIT && CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
-  const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - pr : pr) : pr;
+  const int qt = SPLIT ? pr / splits : (CAUSAL ? (pass == 0 ? n_qtiles - 1 - pr : pr) : pr);
   // every wave is done with the previous tile's LDS slots before this tile's copies start
   if (pass > 0) __syncthreads();
   const int q0 = qt * BM;
@@ -86,12 +96,33 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   const int ntiles = (kv_end + BN - 1) / BN;
   // Tiles [0, n_plain) have every key visible to every row of the workgroup: no mask.
   const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
+  // This workgroup's key tiles [t0, last]: all of them, or its split's share.
+  const int t0 = SPLIT ? (int)((long long)sp * ntiles / splits) : 0;
+  const int t1 = SPLIT ? (int)((long long)(sp + 1) * ntiles / splits) : ntiles;
+  const size_t rows_all = (size_t)BH * N;
+  if (SPLIT && t0 >= t1) {
+    // An empty key range (more splits than tiles): a state that the merge weighs with zero.
+    if (qrow < N) {
+      const size_t r = (size_t)sp * rows_all + (size_t)bh * N + qrow;
+      float* po = part + r * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<f32x4*>(po + db * 32 + 8 * g + 4 * h) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (h == 0) {
+        part[(size_t)splits * rows_all * D + r] = -INFINITY;
+        part[(size_t)splits * rows_all * (D + 1) + r] = 0.f;
+      }
+    }
+    continue;
+  }
+  const int last = t1 - 1;
 
   auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, N, wave); };
   auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, N, wave); };
-  stage_k(0, lds_k0);
-  stage_v(0, lds_v0);
-  stage_k(min(1, ntiles - 1), lds_k1);
+  stage_k(t0, lds_k0);
+  stage_v(t0, lds_v0);
+  stage_k(min(t0 + 1, last), lds_k1);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qrow][16ks + 8h .. +7].
   Frag qf[KS];
@@ -228,12 +259,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   __syncthreads();
   f32x16 s[KB];
   qk(lds_k0, s);
-  if (n_plain == 0) mask(s, 0);
+  if (t0 >= n_plain) mask(s, t0);
   row_max(s);
   // Every wave is done with slot k0 before the first step copies K(2) over it.
   ring_barrier();
 
-  // ---- steps t = 0 .. ntiles-2, slot parity P = t & 1 fixed at compile time.
+  // ---- steps t = t0 .. last-1, slot parity P = (t - t0) & 1 fixed at compile time.
   auto step = [&](auto mask_tag, auto parity_tag, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(parity_tag)::value;
@@ -244,7 +275,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     // Copies of K(t+2) and V(t+1): descriptors now, the copies themselves spread over the
     // chunks of [A] (issued all at once, the workgroup's waves queue behind each other in the
     // texture unit right after the barrier).
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, min(t + 2, ntiles - 1) * BN, N);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, min(t + 2, last) * BN, N);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, BN>(Vh, (t + 1) * BN, N);
     constexpr int CPW = BN * D * 2 / 1024 / NW;  // copies per wave per tile
 
@@ -357,10 +388,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   using Tr = std::true_type;
   using Even = std::integral_constant<int, 0>;
   using Odd = std::integral_constant<int, 1>;
-  const int last = ntiles - 1;
   // Steps whose next tile needs no mask: t + 1 < n_plain.
-  const int plain_steps = max(0, min(n_plain - 1, last));
-  int t = 0;
+  const int plain_steps = max(t0, min(n_plain - 1, last));
+  int t = t0;
   for (; t + 1 < plain_steps; t += 2) {
     step(F(), Even(), t);
     step(F(), Odd(), t + 1);
@@ -369,13 +399,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     step(Tr(), Even(), t);
     if (t + 1 < last) step(Tr(), Odd(), t + 1);
   }
-  if (last & 1)
+  if ((last - t0) & 1)
     drain(Odd());
   else
     drain(Even());
 
   // ---- epilogue: one division per row, store O and LSE
   const float l_tot = half_swap_sum(l_run);
+  if (SPLIT) {
+    if (qrow < N) {
+      const size_t r = (size_t)sp * rows_all + (size_t)bh * N + qrow;
+      float* po = part + r * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(po + db * 32 + 8 * g + 4 * h) =
+              f32x4{acc[db][4 * g + 0], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+      if (h == 0) {
+        part[(size_t)splits * rows_all * D + r] = l_tot > 0.f ? m_ref : -INFINITY;
+        part[(size_t)splits * rows_all * (D + 1) + r] = l_tot;
+      }
+    }
+    continue;
+  }
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
     uint16_t* orow = O + head + (size_t)qrow * D;
@@ -393,15 +440,79 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   }  // pass
 }
 
+// ------------------------------------------------------------------------------------------
+// Merge of the split-KV partial states ("FlashAttentionを1から", section "その後の版と、推論での
+// 事情"; the same algebra as the online softmax update). Per row, with m_s in log2 units:
+//   M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,  O = (sum_s w_s acc_s) / L,
+//   LSE = ln2 * (M + log2 L).
+// An empty state (m_s = -inf, l_s = 0, acc_s = 0) gets weight 0. D/4 threads per row, 4
+// elements each (16-byte loads of the fp32 partials).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ O,
+                                                    float* __restrict__ LSE, long long rows, int splits) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int sub = threadIdx.x % TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= rows) return;
+  const float* pm = part + (size_t)splits * rows * D;
+  const float* pl = pm + (size_t)splits * rows;
+  float M = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, pm[(size_t)sp * rows + row]);
+  const float Mr = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const size_t r = (size_t)sp * rows + row;
+    const float w = __builtin_amdgcn_exp2f(pm[r] - Mr);
+    L = __builtin_fmaf(w, pl[r], L);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(part + r * D + sub * 4);
+    a0 = __builtin_fmaf(w, o[0], a0);
+    a1 = __builtin_fmaf(w, o[1], a1);
+    a2 = __builtin_fmaf(w, o[2], a2);
+    a3 = __builtin_fmaf(w, o[3], a3);
+  }
+  const float inv = 1.0f / L;
+  u32x2 w2;
+  w2[0] = T::pack2(a0 * inv, a1 * inv);
+  w2[1] = T::pack2(a2 * inv, a3 * inv);
+  *reinterpret_cast<u32x2*>(O + row * D + sub * 4) = w2;
+  if (sub == 0 && LSE != nullptr) LSE[row] = (Mr + __log2f(L)) * kLn2;
+}
+
+template <typename T, int D>
+static hipError_t launch_merge_t(const FwdArgs& a) {
+  constexpr int RPB = 256 / (D / 4);
+  const long long rows = (long long)a.BH * a.N;
+  const long long grid = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)a.stream, a.part,
+                     (uint16_t*)a.o, a.lse, rows, a.splits);
+  return hipGetLastError();
+}
+
+static hipError_t launch_merge(const FwdArgs& a) {
+  if (a.bf16) return a.d == 64 ? launch_merge_t<BF16, 64>(a) : launch_merge_t<BF16, 128>(a);
+  return a.d == 64 ? launch_merge_t<FP16, 64>(a) : launch_merge_t<FP16, 128>(a);
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int NW = 4, BN = 64;
   constexpr int BM = NW * 32;
   const int n_qtiles = (a.N + BM - 1) / BM;
+  if (a.splits > 0) {
+    const long long grid = (long long)n_qtiles * a.splits * a.BH;
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (uint16_t*)a.o, a.lse, a.BH, a.N, n_qtiles, a.c_log2, a.part, a.splits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge(a);
+  }
   const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * a.BH;
-  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.BH, a.N, n_qtiles, a.c_log2);
+                     (uint16_t*)a.o, a.lse, a.BH, a.N, n_qtiles, a.c_log2, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@ struct FwdArgs {
   bool causal, bf16;
   float c_log2;  // scale * log2(e)
   void* stream;
+  int splits = 0;         // > 0: split-KV forward with this many key ranges per Q tile
+  float* part = nullptr;  // split-KV partial states (see fwd_kernel), splits > 0 only
 };
 
 struct BwdArgs {

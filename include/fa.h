@@ -51,6 +51,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -76,6 +78,35 @@ typedef enum {
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, int causal, float scale, int dtype,
                void* stream);
+
+/*
+ * Split-KV forward, for grids that would not fill the GPU (few heads, short sequences):
+ * the keys of every 128-row Q tile are cut into `num_splits` contiguous ranges of 64-key
+ * tiles, one workgroup each computes the softmax state (max m, sum l, unnormalised output)
+ * of its range, and a second kernel merges the states -- the combination of partial
+ * (m, l, O~) over disjoint key ranges described in "FlashAttentionを1から", section
+ * "その後の版と、推論での事情". The result is the same exact attention as fa_forward
+ * (same o and lse contract), up to fp32 rounding order.
+ *   num_splits    1 .. 256; ranges beyond a tile's key count are empty and merge with
+ *                 weight zero.
+ *   workspace     device float32 scratch of at least
+ *                 fa_forward_splitkv_workspace_bytes(B, H, N, d, num_splits) bytes,
+ *                 16-byte aligned, not overlapping any other argument; contents on entry
+ *                 are ignored and on return are unspecified.
+ * Two kernel launches on `stream`. Returns an fa_status; a workspace that is NULL,
+ * misaligned, too small or overlapping, or num_splits outside 1..256, is
+ * FA_ERR_INVALID_ARG.
+ */
+int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale, int dtype,
+                       int num_splits, float* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Workspace bytes fa_forward_splitkv needs: num_splits * B*H*N * (d + 2) * 4. Returns 0 for
+ * arguments fa_forward_splitkv would refuse (sizes, head dim, num_splits).
+ */
+size_t fa_forward_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
 
 /*
  * Backward pass.

@@ -113,3 +113,36 @@ def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 1, 16, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.fa_forward(q, q, q, q.clone(), None, False, 0.125)
+
+
+def splitkv(lib, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], ws=A[5], ws_bytes=1 << 30, splits=2, B=1, H=1, N=16,
+            d=64, causal=0, scale=0.125, dtype=0):
+    vp = ctypes.c_void_p
+    return lib.fa_forward_splitkv(vp(q), vp(k), vp(v), vp(o), vp(lse), B, H, N, d, causal, scale, dtype, splits, vp(ws),
+                                  ctypes.c_size_t(ws_bytes), vp(0))
+
+
+def test_splitkv_workspace_bytes(lib):
+    size = fa.fa_forward_splitkv_workspace_bytes
+    assert size(2, 3, 100, 64, 4) == 4 * 2 * 3 * 100 * (64 + 2) * 4
+    assert size(1, 1, 1, 128, 1) == (128 + 2) * 4
+    assert size(1, 1, 16, 64, 0) == 0           # num_splits outside 1..256
+    assert size(1, 1, 16, 64, 257) == 0
+    assert size(1, 1, 16, 96, 2) == 0           # unsupported head dim
+    assert size(0, 1, 16, 64, 2) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=257), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=A[5] + 4), fa.FA_ERR_INVALID_ARG),                   # misaligned workspace
+    (dict(ws_bytes=2 * 16 * (64 + 2) * 4 - 4), fa.FA_ERR_INVALID_ARG),  # one float short
+    (dict(ws=A[0] + 64), fa.FA_ERR_INVALID_ARG),                  # workspace inside q
+    (dict(ws=A[4]), fa.FA_ERR_INVALID_ARG),                       # workspace aliases lse
+    (dict(o=A[1]), fa.FA_ERR_INVALID_ARG),                        # output aliases an input
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARG),
+])
+def test_splitkv_validation(lib, kw, code):
+    assert splitkv(lib, **kw) == code
