@@ -6,10 +6,12 @@ There is no CPU or PyTorch fallback: if libfa.so is missing, or a tensor is not 
 GPU, the call raises.
 
 Raw entry points with the C names (``fa_forward``, ``fa_forward_splitkv``, ``fa_backward``,
-``fa_status_string``, ...)
+``fa_forward_ex``, ``fa_backward_ex``, ``fa_status_string``, ...)
 take torch tensors in the documented layouts and return nothing (they raise
 ``FAError`` on a non-zero status). ``attention_forward`` / ``attention_backward`` allocate
-the outputs with torch and call them; ``FlashAttentionFunction`` wraps both for autograd
+the outputs with torch and call them; ``flash_attention`` (contiguous (B, H, N, d)),
+``flash_attn_func`` ((B, N, H, d) tensors or views with contiguous rows) and
+``flash_attn_varlen_func`` (packed (total, H, d) with ``cu_seqlens``) wrap them for autograd
 (the forward saves Q, K, V, O and LSE only -- "Triton 05: Flash Attention", section
 "torch.autograd.Function 래핑").
 """
@@ -29,7 +31,20 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_splitkv", "fa_forward_splitkv_workspace_bytes", "fa_backward",
-                    "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_status_string")
+                    "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_forward_ex", "fa_backward_ex",
+                    "fa_status_string")
+
+
+class FAStrides(ctypes.Structure):
+    """fa_strides: element strides (batch, head, row) of one operand; the head dim is contiguous."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
+
+
+class FAProblem(ctypes.Structure):
+    """fa_problem: shape, optional device cu_seqlens (variable lengths), mask, scale, dtype."""
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
+                ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int), ("causal", ctypes.c_int),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
 
 _lib = None
 
@@ -63,6 +78,11 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dkv.restype = i
     lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_backward_dq.restype = i
+    S, P = FAStrides, ctypes.POINTER(FAProblem)
+    lib.fa_forward_ex.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, vp]
+    lib.fa_forward_ex.restype = i
+    lib.fa_backward_ex.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp, vp]
+    lib.fa_backward_ex.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -263,3 +283,148 @@ def flash_attention(q, k, v, causal: bool = False, scale: float | None = None):
     if scale is None:
         scale = q.shape[-1] ** -0.5
     return _autograd_function().apply(q, k, v, causal, scale)
+
+
+# ------------------------------------------------- strided operands and variable lengths
+
+LAYOUTS = ("bhnd", "bnhd")
+
+
+def _ex_operand(name, t, shape, dtype, layout, varlen):
+    """fa_strides of a GPU tensor in `layout` ((B,H,N,d), (B,N,H,d), or (total,H,d) packed)."""
+    if t is None:
+        return FAStrides(0, 0, 0)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    st = t.stride()
+    if st[-1] != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous (stride 1)")
+    if varlen:
+        return FAStrides(0, st[1], st[0])
+    if layout == "bhnd":
+        return FAStrides(st[0], st[1], st[2])
+    return FAStrides(st[0], st[2], st[1])
+
+
+def _ex_problem(q, layout, cu_seqlens, max_seqlen, causal, scale):
+    """(problem, operand shape, statistics shape, varlen) of a strided / variable-length call."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {LAYOUTS}")
+    if cu_seqlens is not None:
+        if q.dim() != 3:
+            raise ValueError("with cu_seqlens, q is (total, H, d)")
+        if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous int32 GPU tensor of B+1 offsets")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen (the longest sequence) is required with cu_seqlens")
+        T, H, d = q.shape
+        B = cu_seqlens.numel() - 1
+        prob = FAProblem(B, H, int(max_seqlen), d, ctypes.c_void_p(cu_seqlens.data_ptr()), T, int(bool(causal)),
+                         float(scale), _dtype_code(q))
+        return prob, (T, H, d), (H, T), True
+    if q.dim() != 4:
+        raise ValueError("q is (B, H, N, d) or (B, N, H, d)")
+    if layout == "bhnd":
+        B, H, N, d = q.shape
+    else:
+        B, N, H, d = q.shape
+    prob = FAProblem(B, H, N, d, None, 0, int(bool(causal)), float(scale), _dtype_code(q))
+    return prob, tuple(q.shape), (B, H, N), False
+
+
+def fa_forward_ex(q, k, v, o, lse, causal: bool, scale: float, layout: str = "bnhd", cu_seqlens=None,
+                  max_seqlen=None, stream=None) -> None:
+    """Forward on strided operands: (B,H,N,d) or (B,N,H,d) views whose head dim is contiguous,
+    or, with cu_seqlens (int32, B+1 offsets on the GPU), packed (total, H, d) sequences; lse is
+    (B, H, N) or, with cu_seqlens, (H, total) float32, or None."""
+    import torch
+    prob, shape, sshape, varlen = _ex_problem(q, layout, cu_seqlens, max_seqlen, causal, scale)
+    ops = [_ex_operand(n, t, shape, q.dtype, layout, varlen) for n, t in (("q", q), ("k", k), ("v", v), ("o", o))]
+    if lse is not None:
+        _check_bhnd("lse", lse, sshape, torch.float32)
+    st = load_library().fa_forward_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2], _ptr(o),
+                                      ops[3], _ptr(lse), _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_ex")
+
+
+def fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, causal: bool, scale: float, layout: str = "bnhd",
+                   cu_seqlens=None, max_seqlen=None, stream=None) -> None:
+    """Backward on strided operands / packed sequences (same layouts as fa_forward_ex); delta
+    is a float32 workspace shaped like lse."""
+    import torch
+    prob, shape, sshape, varlen = _ex_problem(q, layout, cu_seqlens, max_seqlen, causal, scale)
+    names = (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv))
+    ops = [_ex_operand(n, t, shape, q.dtype, layout, varlen) for n, t in names]
+    for name, t in (("lse", lse), ("delta", delta)):
+        _check_bhnd(name, t, sshape, torch.float32)
+    st = load_library().fa_backward_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2],
+                                       _ptr(o), ops[3], _ptr(do), ops[4], _ptr(lse), _ptr(dq), ops[5], _ptr(dk),
+                                       ops[6], _ptr(dv), ops[7], _ptr(delta), _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_backward_ex")
+
+
+def _row_major(t):
+    return t if t.stride(-1) == 1 else t.contiguous()
+
+
+_AUTOGRAD_EX = None
+
+
+def _autograd_function_ex():
+    global _AUTOGRAD_EX
+    if _AUTOGRAD_EX is not None:
+        return _AUTOGRAD_EX
+    import torch
+
+    class FlashAttentionExFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale, cu_seqlens, max_seqlen):
+            q, k, v = _row_major(q), _row_major(k), _row_major(v)
+            o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+            if cu_seqlens is None:
+                B, N, H, _ = q.shape
+                lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+            else:
+                lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+            fa_forward_ex(q, k, v, o, lse, causal, scale, "bnhd", cu_seqlens, max_seqlen)
+            ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
+            ctx.causal, ctx.scale, ctx.max_seqlen = causal, scale, max_seqlen
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse, cu_seqlens = ctx.saved_tensors
+            do = _row_major(do)
+            dq, dk, dv = (torch.empty(t.shape, dtype=t.dtype, device=t.device) for t in (q, k, v))
+            delta = torch.empty_like(lse)
+            fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, ctx.causal, ctx.scale, "bnhd", cu_seqlens,
+                           ctx.max_seqlen)
+            return dq, dk, dv, None, None, None, None
+
+    _AUTOGRAD_EX = FlashAttentionExFunction
+    return FlashAttentionExFunction
+
+
+def flash_attn_func(q, k, v, causal: bool = False, scale: float | None = None):
+    """Differentiable exact attention on (B, N, H, d) GPU tensors (any strides with a
+    contiguous head dim, e.g. slices of a packed (B, N, 3, H, d) tensor)."""
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _autograd_function_ex().apply(q, k, v, causal, scale, None, None)
+
+
+def flash_attn_varlen_func(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None):
+    """Differentiable exact attention over packed variable-length sequences: q, k, v are
+    (total, H, d) GPU tensors, sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1] - 1
+    (int32 GPU tensor of B+1 offsets), max_seqlen bounds every length. Each sequence attends
+    only to itself ("FlashAttentionを1から", section "現場ではこう使う")."""
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _autograd_function_ex().apply(q, k, v, causal, scale, cu_seqlens, int(max_seqlen))

@@ -20,19 +20,22 @@
 namespace fa {
 
 // ------------------------------------------------------------------------------------------
-// [1] D_i = sum_c dO_ic * O_ic, fp32 accumulation, from the stored (rounded) O.
+// [1] D_i = sum_c dO_ic * O_ic, fp32 accumulation, from the stored (rounded) O. A block covers
+// RPB consecutive rows of one statistics head (nrb blocks per head).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __restrict__ O,
                                                              const uint16_t* __restrict__ dO,
-                                                             float* __restrict__ delta, long long rows) {
+                                                             float* __restrict__ delta, Geom geo, Strides so,
+                                                             Strides sdo, int nrb) {
   constexpr int TPR = D / 8;       // threads per row (16 B each)
-  constexpr int RPB = 256 / TPR;   // rows per block per pass
+  constexpr int RPB = 256 / TPR;   // rows per block
   const int sub = threadIdx.x % TPR;
-  long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const long long step = (long long)gridDim.x * RPB;
-  for (; row < rows; row += step) {
-    const u32x4 o = *reinterpret_cast<const u32x4*>(O + row * D + sub * 8);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + sub * 8);
+  const int hh = blockIdx.x / nrb;
+  const int r = (blockIdx.x - hh * nrb) * RPB + threadIdx.x / TPR;
+  // whole rows (TPR consecutive lanes) leave together, so the shuffles below stay in-row
+  if (r < stat_rows(geo)) {
+    const u32x4 o = *reinterpret_cast<const u32x4*>(O + stat_row_offset(geo, so, hh, r) + sub * 8);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + stat_row_offset(geo, sdo, hh, r) + sub * 8);
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -41,7 +44,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
     }
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (sub == 0) delta[row] = s;
+    if (sub == 0) delta[(long long)hh * stat_rows(geo) + r] = s;
   }
 }
 
@@ -61,7 +64,8 @@ template <typename T, int D, int BN, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dQ, int BH, int N, int n_qtiles, float scale, float c_log2) {
+    uint16_t* __restrict__ dQ, Geom geo, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdq,
+    int n_qtiles_max, float scale, float c_log2) {
   constexpr int KB = BN / 32;  // 32-key blocks per K/V tile
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;
@@ -86,21 +90,29 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   // Causal: a workgroup takes the pair of Q tiles (n_qtiles-1-p, p), the heavy one first, so
   // every workgroup has the same number of K/V tiles; an odd middle tile runs alone. A head's
   // workgroups run together on one XCD (shared K/V reads in its L2).
-  const int npairs = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  // The grid covers the longest sequence; a workgroup past its own sequence's tiles exits.
+  const int BH = geo.B * geo.H;
+  const int npairs = CAUSAL ? (n_qtiles_max + 1) / 2 : n_qtiles_max;
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
+  const Seq sq_ = seq_of(geo, bh);
+  const int N = sq_.n;
+  const int n_qtiles = (N + BM - 1) / BM;
+  if (pr >= (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles)) return;
   const int npass = (CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
+  const uint16_t* Qh = seq_base(Q, sq, sq_);
+  const uint16_t* Kh = seq_base(K, sk, sq_);
+  const uint16_t* Vh = seq_base(V, sv, sq_);
+  const uint16_t* dOh = seq_base(dO, sdo, sq_);
+  uint16_t* dQh = seq_base(dQ, sdq, sq_);
+  const int rsq = (int)sq.r, rsk = (int)sk.r, rsv = (int)sv.r, rsdo = (int)sdo.r, rsdq = (int)sdq.r;
   for (int pass = 0; pass < npass; ++pass) {
   const int qt = CAUSAL ? (pass == 0 ? n_qtiles - 1 - pr : pr) : pr;
   // every wave is done with the previous tile's LDS slots before this tile's copies start
   if (pass > 0) __syncthreads();
   const int q0 = qt * BM;
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row
-
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
@@ -109,8 +121,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   // Keys past N, and with the causal mask keys after the row, are hidden: key <= key_lim.
   const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 
-  stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, N, wave);
-  stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, N, wave);
+  stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, N, rsk, wave);
+  stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, N, rsv, wave);
 
   Frag qf[KS], dof[KS];
   float lse2, dl;
@@ -118,11 +130,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     const bool ok = qrow < N;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[ks].v = gload16(Q + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
-      dof[ks].v = gload16(dO + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
+      qf[ks].v = gload16(Qh + (size_t)qrow * rsq + ks * 16 + h * 8, ok);
+      dof[ks].v = gload16(dOh + (size_t)qrow * rsdo + ks * 16 + h * 8, ok);
     }
-    lse2 = ok ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
-    dl = ok ? Delta[(size_t)bh * N + qrow] : 0.f;
+    lse2 = ok ? LSE[sq_.stat + qrow] * kLog2e : 0.f;
+    dl = ok ? Delta[sq_.stat + qrow] : 0.f;
   }
 
   f32x16 acc[DB];
@@ -163,8 +175,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     // this lane's row iff key <= key_lim, i.e. iff its compile-time offset is <= thr.
     const int thr = key_lim - t * BN - 4 * h;
     const int tn = min(t + 1, ntiles - 1);
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, tn * BN, N);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, BN>(Vh, tn * BN, N);
+    const TileSrc rk = tile_src<D, BN>(Kh, tn * BN, N, rsk);
+    const TileSrc rv = tile_src<D, BN>(Vh, tn * BN, N, rsv);
     // fragment i of a K or V tile: key block i % KB (so consecutive MFMAs are independent),
     // k-step i / KB
     auto rfrag = [&](const uint16_t* tile, int i) {
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   wait_async();
 
   if (qrow < N) {
-    uint16_t* row = dQ + head + (size_t)qrow * D;
+    uint16_t* row = dQh + (size_t)qrow * rsdq;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -298,11 +310,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
 template <typename T, int D>
 static hipError_t launch_pre_t(const BwdArgs& a) {
   constexpr int RPB = 256 / (D / 8);
-  const long long rows = (long long)a.BH * a.N;
-  long long blocks = (rows + RPB - 1) / RPB;
-  if (blocks > 8192) blocks = 8192;
+  const int nrb = (stat_rows(a.g) + RPB - 1) / RPB;
+  const long long blocks = (long long)stat_heads(a.g) * nrb;
+  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.o, (const uint16_t*)a.dO, a.delta, rows);
+                     (const uint16_t*)a.o, (const uint16_t*)a.dO, a.delta, a.g, a.so, a.sdo, nrb);
   return hipGetLastError();
 }
 
@@ -310,12 +322,13 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a) {
   constexpr int NW = 4, BN = 64;
   constexpr int BM = NW * 32;
-  const int n_qtiles = (a.N + BM - 1) / BM;
-  const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * a.BH;
+  const int n_qtiles = (a.g.N + BM - 1) / BM;
+  const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * a.g.B * a.g.H;
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dq, a.BH, a.N, n_qtiles, a.scale,
-                     a.c_log2);
+                     (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dq, a.g, a.sq, a.sk, a.sv, a.sdo, a.sdq,
+                     n_qtiles, a.scale, a.c_log2);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ template <typename T, int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale, float c_log2) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, Geom geo, Strides sq, Strides sk, Strides sv,
+    Strides sdo, Strides sdk, Strides sdv, int n_ktiles_max, float scale, float c_log2) {
   constexpr int BK = NW * 32;
   constexpr int BQ = 32;
   constexpr int KS = D / 16;
@@ -63,12 +64,26 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   // (p, n_ktiles-1-p), the heavy one first, so every workgroup streams the same number of Q
   // tiles; an odd middle tile runs alone. A head's workgroups run together on one XCD (shared
   // Q/dO reads in its L2).
-  const int n_ktiles = (N + BK - 1) / BK;
-  const int npairs = CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles;
+  // The grid covers the longest sequence; a workgroup past its own sequence's tiles exits.
+  const int BH = geo.B * geo.H;
+  const int npairs = CAUSAL ? (n_ktiles_max + 1) / 2 : n_ktiles_max;
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
+  const Seq sq_ = seq_of(geo, bh);
+  const int N = sq_.n;
+  const int n_ktiles = (N + BK - 1) / BK;
+  if (pr >= (CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles)) return;
   const int npass = (CAUSAL && n_ktiles - 1 - pr != pr) ? 2 : 1;
+  const uint16_t* Qh = seq_base(Q, sq, sq_);
+  const uint16_t* Kh = seq_base(K, sk, sq_);
+  const uint16_t* Vh = seq_base(V, sv, sq_);
+  const uint16_t* dOh = seq_base(dO, sdo, sq_);
+  uint16_t* dKh = seq_base(dK, sdk, sq_);
+  uint16_t* dVh = seq_base(dV, sdv, sq_);
+  const int rsq = (int)sq.r, rsk = (int)sk.r, rsv = (int)sv.r, rsdo = (int)sdo.r;
+  const float* lse_h = LSE + sq_.stat;
+  const float* dl_h = Delta + sq_.stat;
   for (int pass = 0; pass < npass; ++pass) {
   const int kt = pass == 0 ? pr : n_ktiles - 1 - pr;
   // every wave is done with the previous tile's LDS slots before this tile's copies start
@@ -77,18 +92,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* dOh = dO + head;
-  const float* lse_h = LSE + (size_t)bh * N;
-  const float* dl_h = Delta + (size_t)bh * N;
 
   const int it_begin = CAUSAL ? (k0 / BQ) : 0;
   const int it_end = (N + BQ - 1) / BQ;
 
-  stage_rows_swz_buf<D, BK, NW>(lds_v, V + head, k0, N, wave);
-  stage_rows_swz_buf<D, BQ, NW>(lds_q0, Qh, it_begin * BQ, N, wave);
-  stage_rows_swz_buf<D, BQ, NW>(lds_do0, dOh, it_begin * BQ, N, wave);
+  stage_rows_swz_buf<D, BK, NW, true>(lds_v, Vh, k0, N, rsv, wave);
+  stage_rows_swz_buf<D, BQ, NW, true>(lds_q0, Qh, it_begin * BQ, N, rsq, wave);
+  stage_rows_swz_buf<D, BQ, NW, true>(lds_do0, dOh, it_begin * BQ, N, rsdo, wave);
   if (wave == NW - 1) stage_stats_buf(lds_st0, lse_h, dl_h, it_begin * BQ, N);
 
   // Pinned K fragments (B operand of S = Q K^T): lane holds K[key][16ks + 8h .. +7].
@@ -96,7 +106,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   {
     const bool ok = key < N;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks].v = gload16(K + head + (size_t)key * D + ks * 16 + h * 8, ok);
+    for (int ks = 0; ks < KS; ++ks) kf[ks].v = gload16(Kh + (size_t)key * rsk + ks * 16 + h * 8, ok);
   }
   f32x16 acc_dk[DB], acc_dv[DB];
 #pragma unroll
@@ -147,8 +157,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
     int vrow = wave * 32 * D * 2;
     asm volatile("" : "+v"(vrow));
     const int itn = min(it + 1, it_end - 1);
-    const __amdgpu_buffer_rsrc_t rq = tile_rsrc<D, BQ>(Qh, itn * BQ, N);
-    const __amdgpu_buffer_rsrc_t rdo = tile_rsrc<D, BQ>(dOh, itn * BQ, N);
+    const TileSrc rq = tile_src<D, BQ>(Qh, itn * BQ, N, rsq);
+    const TileSrc rdo = tile_src<D, BQ>(dOh, itn * BQ, N, rsdo);
     if (wave == NW - 1) stage_stats_buf(stn, lse_h, dl_h, itn * BQ, N);
 
     // this lane's LSE (then D) values for register group g (rows 8g + 4h .. +3), each read
@@ -171,9 +181,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
         if (ks % GAP == 0) {
           const int c = ks / GAP;
           if (c < CPW)
-            stage_copy<D, BQ, NW>(qn, rq, wave, c);
+            stage_copy<D, BQ, NW, true>(qn, rq, wave, c);
           else
-            stage_copy<D, BQ, NW>(don, rdo, wave, c - CPW);
+            stage_copy<D, BQ, NW, true>(don, rdo, wave, c - CPW);
         }
         if (ks + 2 < KS) qfr[(ks + 2) % 3] = lds_read_rows(qs, rofs[ks + 2]);
         __builtin_amdgcn_sched_barrier(0);
@@ -279,8 +289,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   wait_async();
 
   if (key < N) {
-    uint16_t* dk_row = dK + head + (size_t)key * D;
-    uint16_t* dv_row = dV + head + (size_t)key * D;
+    uint16_t* dk_row = dKh + (size_t)key * sdk.r;
+    uint16_t* dv_row = dVh + (size_t)key * sdv.r;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -301,12 +311,13 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dkv_t(const BwdArgs& a) {
   constexpr int NW = 4;
   constexpr int BK = NW * 32;
-  const int n_ktiles = (a.N + BK - 1) / BK;
-  const long long grid = (long long)(CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles) * a.BH;
+  const int n_ktiles = (a.g.N + BK - 1) / BK;
+  const long long grid = (long long)(CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles) * a.g.B * a.g.H;
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.BH, a.N, a.scale,
-                     a.c_log2);
+                     (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.g, a.sq, a.sk, a.sv,
+                     a.sdo, a.sdk, a.sdv, n_ktiles, a.scale, a.c_log2);
   return hipGetLastError();
 }
 

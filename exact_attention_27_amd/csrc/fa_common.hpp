@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_kernels.hpp"
+
 namespace fa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -270,35 +272,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), (short)0,
                                            __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
-// Descriptor of the rows [grow0, grow0 + ROWS) of a head that exist (n_rows rows in all).
+// Source of a ROWS-row tile: one descriptor over rows [grow0, grow0 + ROWS) of a head whose
+// rows are rs elements apart, ending with the last existing row's D elements (empty if none
+// exists), so every row at or past n_rows reads as zero. Wave-uniform.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int rs;
+};
 template <int D, int ROWS>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* head, int grow0, int n_rows) {
+__device__ __forceinline__ TileSrc tile_src(const uint16_t* head, int grow0, int n_rows, int rs) {
+  TileSrc t;
   const int avail = __builtin_amdgcn_readfirstlane(max(0, min(n_rows - grow0, ROWS)));
-  return make_rsrc(head + (size_t)grow0 * D, avail * D * 2);
+  t.rsrc = make_rsrc(head + (size_t)grow0 * rs, avail > 0 ? ((avail - 1) * rs + D) * 2 : 0);
+  t.rs = rs;
+  return t;
 }
 // Copy k (0 <= k < ROWS*D*2/1024/NW) of wave `wave`'s share of a ROWS-row tile of D 16-bit
-// elements: 1 KB, i.e. 1024/(2D) whole rows, landing swizzled at tile[ins * 512 ...],
-// ins = wave + k*NW. Every wave issues the same, compile-time number of copies, so the
-// compiler's vmcnt bookkeeping is exact.
-template <int D, int ROWS, int NW>
-__device__ __forceinline__ void stage_copy(uint16_t* tile, __amdgpu_buffer_rsrc_t rsrc, int wave, int k) {
+// elements: 1 KB, i.e. RPI = 1024/(2D) whole rows starting at row ins*RPI, ins = wave + k*NW,
+// landing swizzled at tile[ins * 512 ...]. The per-lane part of the source offset (row within
+// the copy, swizzled chunk) is the same for every copy of a wave, because successive copies
+// move by NW*RPI rows, a whole number of swizzle periods; the copy's row shift is added per
+// issue (the hardware range check sees the whole offset). The compiler hoists each copy's
+// sum out of the loop (one register per copy); with SHARED_OFS the lane part is made opaque
+// instead, so one register serves every copy at the price of an add (and a move) per issue,
+// for kernels without registers to spare. Every wave issues the same, compile-time number of
+// copies, so the compiler's vmcnt bookkeeping is exact.
+template <int D, int ROWS, int NW, bool SHARED_OFS = false>
+__device__ __forceinline__ void stage_copy(uint16_t* tile, const TileSrc& src, int wave, int k) {
   constexpr int ROW_BYTES = D * 2;
+  constexpr int RPI = 1024 / ROW_BYTES;  // rows per copy
+  constexpr int LPR = ROW_BYTES / 16;    // lanes per row
   static_assert((ROWS * ROW_BYTES / 1024) % NW == 0, "tile copies must split evenly over the waves");
-  const int l = lane_id();
+  static_assert((NW * RPI) % 16 == 0, "a wave's copies must sit whole swizzle periods (16 rows) apart");
   const int ins = wave + k * NW;
-  const int p = ins * 1024 + l * 16;
-  const int row = p / ROW_BYTES;
-  const int lchunk = ((p % ROW_BYTES) >> 4) ^ swz<D>(row);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void*)(tile + ins * 512), 16, row * ROW_BYTES + lchunk * 16, 0,
-                                           0, 0);
+  const int l = lane_id();
+  const int lrow = l / LPR;
+  int lane_ofs = lrow * src.rs * 2 + (((l % LPR) ^ swz<D>(wave * RPI + lrow)) << 4);  // swz(ins*RPI + lrow)
+  if (SHARED_OFS) asm volatile("" : "+v"(lane_ofs));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc, (FA_LDS void*)(tile + ins * 512), 16,
+                                           lane_ofs + ins * (RPI * 2) * src.rs, 0, 0, 0);
 }
 // All of wave `wave`'s copies of the tile at rows [grow0, grow0 + ROWS).
-template <int D, int ROWS, int NW>
-__device__ __forceinline__ void stage_rows_swz_buf(uint16_t* tile, const uint16_t* head, int grow0, int n_rows,
+template <int D, int ROWS, int NW, bool SHARED_OFS = false>
+__device__ __forceinline__ void stage_rows_swz_buf(uint16_t* tile, const uint16_t* head, int grow0, int n_rows, int rs,
                                                    int wave) {
-  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc<D, ROWS>(head, grow0, n_rows);
+  const TileSrc src = tile_src<D, ROWS>(head, grow0, n_rows, rs);
 #pragma unroll
-  for (int k = 0; k < ROWS * D * 2 / 1024 / NW; ++k) stage_copy<D, ROWS, NW>(tile, rsrc, wave, k);
+  for (int k = 0; k < ROWS * D * 2 / 1024 / NW; ++k) stage_copy<D, ROWS, NW, SHARED_OFS>(tile, src, wave, k);
 }
 
 // Per-row statistics of 32 rows from two arrays: dst[0..31] = a[r0 ..], dst[64..95] =
@@ -367,5 +387,47 @@ constexpr int kSchedTrans = 0x400;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// The sequence a workgroup works on: head bh = b*H + h of the grid, its length n, the packed
+// row its row 0 is (0 for fixed lengths) and the index of its row 0 in LSE / delta. Values
+// read from cu are clamped (0 <= row0 <= row0 + n <= T, n <= N) and made wave-uniform.
+struct Seq {
+  int b, h, n;
+  long long row0, stat;
+};
+__device__ __forceinline__ Seq seq_of(const Geom& g, int bh) {
+  Seq s;
+  s.b = __builtin_amdgcn_readfirstlane(bh / g.H);
+  s.h = __builtin_amdgcn_readfirstlane(bh - s.b * g.H);
+  if (g.cu != nullptr) {
+    const int c0 = min(max(__builtin_amdgcn_readfirstlane(g.cu[s.b]), 0), g.T);
+    const int c1 = min(max(__builtin_amdgcn_readfirstlane(g.cu[s.b + 1]), c0), g.T);
+    s.n = min(c1 - c0, g.N);
+    s.row0 = c0;
+    s.stat = (long long)s.h * g.T + c0;
+  } else {
+    s.n = g.N;
+    s.row0 = 0;
+    s.stat = (long long)bh * g.N;
+  }
+  return s;
+}
+// Row 0 of operand `base` (strides st) for sequence s (with variable lengths the caller
+// passes a zero batch stride: the packed row row0 already selects the sequence).
+template <typename P>
+__device__ __forceinline__ P* seq_base(P* base, const Strides& st, const Seq& s) {
+  return base + ((long long)s.b * st.b + (long long)s.h * st.h + s.row0 * st.r);
+}
+
+// Statistics rows (LSE, delta, split-KV partial states) form (HH, Rh): HH = B*H heads of N
+// rows each (fixed lengths) or H heads of T packed rows (variable lengths); see Geom.
+__host__ __device__ __forceinline__ int stat_heads(const Geom& g) { return g.cu != nullptr ? g.H : g.B * g.H; }
+__host__ __device__ __forceinline__ int stat_rows(const Geom& g) { return g.cu != nullptr ? g.T : g.N; }
+// Element offset of statistics row (hh, r) in an operand with strides st.
+__device__ __forceinline__ long long stat_row_offset(const Geom& g, const Strides& st, int hh, int r) {
+  if (g.cu != nullptr) return (long long)hh * st.h + (long long)r * st.r;
+  const int b = hh / g.H;
+  return (long long)b * st.b + (long long)(hh - b * g.H) * st.h + (long long)r * st.r;
+}
 
 }  // namespace fa

@@ -49,8 +49,8 @@ constexpr float kTau = 8.0f;
 template <typename T, int D, int BN, int NW, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, int n_qtiles, float c_log2,
-    float* __restrict__ part, int splits) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, Geom geo, Strides sq, Strides sk, Strides sv, Strides so,
+    int n_qtiles_max, float c_log2, float* __restrict__ part, long long rows_all, int splits) {
   constexpr int BM = NW * 32;  // query rows per workgroup
   constexpr int KS = D / 16;   // k-steps over the head dim
   constexpr int DB = D / 32;   // 32-wide blocks of the head dim
@@ -75,22 +75,29 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   // end of the grid); an odd middle tile runs alone. A head's workgroups run together on one
   // XCD (shared K/V reads in its L2).
   // Split-KV: one workgroup per (head, Q tile, key range), no pairing.
-  const int npairs = SPLIT ? n_qtiles * splits : (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles);
+  // The grid covers the longest sequence; a workgroup past its own sequence's tiles exits.
+  const int BH = geo.B * geo.H;
+  const int npairs = SPLIT ? n_qtiles_max * splits : (CAUSAL ? (n_qtiles_max + 1) / 2 : n_qtiles_max);
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
+  const Seq sq_ = seq_of(geo, bh);
+  const int N = sq_.n;
+  const int n_qtiles = (N + BM - 1) / BM;
   const int sp = SPLIT ? pr % splits : 0;  // key range of this workgroup
+  if (SPLIT ? pr / splits >= n_qtiles : pr >= (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles)) return;
   const int npass = (!SPLIT && CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
+  const uint16_t* Qh = seq_base(Q, sq, sq_);
+  const uint16_t* Kh = seq_base(K, sk, sq_);
+  const uint16_t* Vh = seq_base(V, sv, sq_);
+  uint16_t* Oh = seq_base(O, so, sq_);
+  const int rsq = (int)sq.r, rsk = (int)sk.r, rsv = (int)sv.r, rso = (int)so.r;
   for (int pass = 0; pass < npass; ++pass) {
   const int qt = SPLIT ? pr / splits : (CAUSAL ? (pass == 0 ? n_qtiles - 1 - pr : pr) : pr);
   // every wave is done with the previous tile's LDS slots before this tile's copies start
   if (pass > 0) __syncthreads();
   const int q0 = qt * BM;
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row
-
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
@@ -99,11 +106,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   // This workgroup's key tiles [t0, last]: all of them, or its split's share.
   const int t0 = SPLIT ? (int)((long long)sp * ntiles / splits) : 0;
   const int t1 = SPLIT ? (int)((long long)(sp + 1) * ntiles / splits) : ntiles;
-  const size_t rows_all = (size_t)BH * N;
   if (SPLIT && t0 >= t1) {
     // An empty key range (more splits than tiles): a state that the merge weighs with zero.
     if (qrow < N) {
-      const size_t r = (size_t)sp * rows_all + (size_t)bh * N + qrow;
+      const size_t r = (size_t)sp * rows_all + sq_.stat + qrow;
       float* po = part + r * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -118,8 +124,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   }
   const int last = t1 - 1;
 
-  auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, N, wave); };
-  auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, N, wave); };
+  auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, N, rsk, wave); };
+  auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, N, rsv, wave); };
   stage_k(t0, lds_k0);
   stage_v(t0, lds_v0);
   stage_k(min(t0 + 1, last), lds_k1);
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   {
     const bool ok = qrow < N;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks].v = gload16(Q + head + (size_t)qrow * D + ks * 16 + h * 8, ok);
+    for (int ks = 0; ks < KS; ++ks) qf[ks].v = gload16(Qh + (size_t)qrow * rsq + ks * 16 + h * 8, ok);
   }
 
   f32x16 acc[DB];
@@ -275,8 +281,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     // Copies of K(t+2) and V(t+1): descriptors now, the copies themselves spread over the
     // chunks of [A] (issued all at once, the workgroup's waves queue behind each other in the
     // texture unit right after the barrier).
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D, BN>(Kh, min(t + 2, last) * BN, N);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D, BN>(Vh, (t + 1) * BN, N);
+    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 2, last) * BN, N, rsk);
+    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, N, rsv);
     constexpr int CPW = BN * D * 2 / 1024 / NW;  // copies per wave per tile
 
     // [A] S(t+1) on the matrix cores while the VALU exponentiates S(t). Written out as 16
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   const float l_tot = half_swap_sum(l_run);
   if (SPLIT) {
     if (qrow < N) {
-      const size_t r = (size_t)sp * rows_all + (size_t)bh * N + qrow;
+      const size_t r = (size_t)sp * rows_all + sq_.stat + qrow;
       float* po = part + r * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   }
   const float inv = 1.0f / l_tot;
   if (qrow < N) {
-    uint16_t* orow = O + head + (size_t)qrow * D;
+    uint16_t* orow = Oh + (size_t)qrow * rso;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -435,7 +441,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
         w[1] = T::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
       }
-    if (LSE != nullptr && h == 0) LSE[(size_t)bh * N + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+    if (LSE != nullptr && h == 0) LSE[sq_.stat + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
   }
   }  // pass
 }
@@ -446,15 +452,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
 //   M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,  O = (sum_s w_s acc_s) / L,
 //   LSE = ln2 * (M + log2 L).
 // An empty state (m_s = -inf, l_s = 0, acc_s = 0) gets weight 0. D/4 threads per row, 4
-// elements each (16-byte loads of the fp32 partials).
+// elements each (16-byte loads of the fp32 partials); a block covers RPB consecutive rows of
+// one statistics head (nrb blocks per head).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ O,
-                                                    float* __restrict__ LSE, long long rows, int splits) {
+                                                    float* __restrict__ LSE, Geom geo, Strides so, long long rows,
+                                                    int nrb, int splits) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
   const int sub = threadIdx.x % TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  if (row >= rows) return;
+  const int hh = blockIdx.x / nrb;
+  const int r = (blockIdx.x - hh * nrb) * RPB + threadIdx.x / TPR;
+  if (r >= stat_rows(geo)) return;
+  const long long row = (long long)hh * stat_rows(geo) + r;
   const float* pm = part + (size_t)splits * rows * D;
   const float* pl = pm + (size_t)splits * rows;
   float M = -INFINITY;
@@ -476,17 +486,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   u32x2 w2;
   w2[0] = T::pack2(a0 * inv, a1 * inv);
   w2[1] = T::pack2(a2 * inv, a3 * inv);
-  *reinterpret_cast<u32x2*>(O + row * D + sub * 4) = w2;
+  *reinterpret_cast<u32x2*>(O + stat_row_offset(geo, so, hh, r) + sub * 4) = w2;
   if (sub == 0 && LSE != nullptr) LSE[row] = (Mr + __log2f(L)) * kLn2;
 }
 
 template <typename T, int D>
 static hipError_t launch_merge_t(const FwdArgs& a) {
   constexpr int RPB = 256 / (D / 4);
-  const long long rows = (long long)a.BH * a.N;
-  const long long grid = (rows + RPB - 1) / RPB;
+  const long long rows = (long long)stat_heads(a.g) * stat_rows(a.g);
+  const int nrb = (stat_rows(a.g) + RPB - 1) / RPB;
+  const long long grid = (long long)stat_heads(a.g) * nrb;
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)a.stream, a.part,
-                     (uint16_t*)a.o, a.lse, rows, a.splits);
+                     (uint16_t*)a.o, a.lse, a.g, a.so, rows, nrb, a.splits);
   return hipGetLastError();
 }
 
@@ -499,20 +511,25 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int NW = 4, BN = 64;
   constexpr int BM = NW * 32;
-  const int n_qtiles = (a.N + BM - 1) / BM;
+  const int n_qtiles = (a.g.N + BM - 1) / BM;
+  const int BH = a.g.B * a.g.H;
   if (a.splits > 0) {
-    const long long grid = (long long)n_qtiles * a.splits * a.BH;
-    hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.BH, a.N, n_qtiles, a.c_log2, a.part, a.splits);
+    const long long grid = (long long)n_qtiles * a.splits * BH;
+    const long long rows_all = (long long)stat_heads(a.g) * stat_rows(a.g);
+    if (grid > 0)
+      hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                         (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                         (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, a.c_log2, a.part, rows_all,
+                         a.splits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge(a);
   }
-  const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * a.BH;
+  const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * BH;
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.BH, a.N, n_qtiles, a.c_log2, nullptr, 0);
+                     (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, a.c_log2, nullptr, 0LL, 0);
   return hipGetLastError();
 }
 

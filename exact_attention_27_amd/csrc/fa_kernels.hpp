@@ -6,13 +6,34 @@
 
 namespace fa {
 
+// Element strides of one (B, H, N, d) operand: element (b, h, r, c) sits at
+// base + b*b + h*h + r*r + c (the d elements of a row are contiguous). With variable-length
+// sequences the batch stride is unused: row r of sequence b is row cu[b] + r of the packed
+// operand.
+struct Strides {
+  long long b, h, r;
+};
+
+// Problem geometry. Fixed length (cu == nullptr): every sequence has N rows and LSE / delta
+// are (B, H, N) contiguous. Variable length: sequence b is rows [cu[b], cu[b+1]) of every
+// operand, N bounds every length, T is the number of rows in all, and LSE / delta are (H, T)
+// contiguous. A workgroup clamps what it reads from cu to [0, T] and lengths to N, so no
+// contents of cu lead it outside the operands.
+struct Geom {
+  int B, H, N;
+  const int* cu;
+  int T;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;  // may be null
-  int BH, N, d;
+  Strides sq, sk, sv, so;
+  Geom g;
+  int d;
   bool causal, bf16;
   float c_log2;  // scale * log2(e)
   void* stream;
@@ -31,7 +52,9 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;
-  int BH, N, d;
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  Geom g;
+  int d;
   bool causal, bf16;
   float scale;
   float c_log2;

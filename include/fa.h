@@ -21,7 +21,8 @@
  *
  *   Layout     Q, K, V, O, dO, dQ, dK, dV are contiguous row-major (B, H, N, d)
  *              tensors of the element type `dtype`; LSE and delta are contiguous
- *              (B, H, N) float32. No strides.
+ *              (B, H, N) float32. fa_forward_ex / fa_backward_ex (end of this file)
+ *              also take strided operands and variable-length batches.
  *   Types      dtype FA_FP16 (IEEE binary16) or FA_BF16 (bfloat16). Arithmetic is
  *              fp32 inside (fp32 accumulation on the matrix cores); every fp32 ->
  *              16-bit conversion rounds to nearest even.
@@ -144,6 +145,62 @@ int fa_backward_dkv(const void* q, const void* k, const void* v, const void* dO,
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                    const float* delta, void* dq, int B, int H, int N, int d, int causal, float scale,
                    int dtype, void* stream);
+
+/*
+ * Strided operands and variable-length batches.
+ *
+ * fa_strides: element strides of one operand. Element (b, h, r, c) of a (B, H, N, d)
+ *   operand sits at data + b*batch + h*head + r*row + c: the d elements of a row are
+ *   contiguous, the rest is the caller's choice. Examples: (B, H, N, d) storage is
+ *   {H*N*d, N*d, d}; (B, N, H, d) storage is {N*H*d, d, H*d}; Q, K, V packed
+ *   as (B, N, 3, H, d) share {3*N*H*d, d, 3*H*d} with data pointers H*d elements apart.
+ *   Every stride is >= 0 and a multiple of 8 elements (16 bytes); row lies in [d, 2^23].
+ *
+ * fa_problem: the shape of one call.
+ *   B, H, d, causal, scale, dtype  as for fa_forward().
+ *   cu_seqlens == NULL  every sequence has N rows; lse and delta are (B, H, N) float32.
+ *   cu_seqlens != NULL  variable lengths ("FlashAttentionを1から", section "現場ではこう使う":
+ *       padding every sequence to the longest pays for the padding; cumulative sequence
+ *       offsets avoid it). A DEVICE array of B+1 int32 with
+ *       0 = cu[0] <= cu[1] <= ... <= cu[B] = total: sequence b is the packed rows
+ *       [cu[b], cu[b+1]) of every operand (each operand holds `total` rows of H heads; the
+ *       batch stride is ignored). N is an upper bound of every length (the grid is sized
+ *       by it); lse and delta are (H, total) float32. Each sequence attends only to itself,
+ *       with the causal mask top-left aligned within it. The library never reads
+ *       cu_seqlens on the host: offsets outside [0, total] are clamped and lengths above
+ *       N cut to N on the device, so no contents make a kernel read or write outside the
+ *       operands, but a batch that breaks the rules above gets unspecified values.
+ *       total may be 0 (nothing is enqueued).
+ *
+ * Overlap rules: outputs (o, lse; dq, dk, dv, delta) must address every element once
+ * (injective strides) and share no element with any input or with each other. Inputs may
+ * overlap each other. Two operands with equal strides are tested element-exactly (so the
+ * three slices of one packed (B, N, 3, H, d) gradient are accepted as separate outputs);
+ * otherwise their address ranges must not intersect.
+ */
+typedef struct {
+  long long batch, head, row;
+} fa_strides;
+
+typedef struct {
+  int B, H, N, d;
+  const int* cu_seqlens;
+  int total;
+  int causal;
+  float scale;
+  int dtype;
+} fa_problem;
+
+/* fa_forward() on strided operands / variable-length batches (rules above). */
+int fa_forward_ex(const fa_problem* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                  const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* stream);
+
+/* fa_backward() on strided operands / variable-length batches (rules above): the same three
+ * kernels in the same order on `stream`. */
+int fa_backward_ex(const fa_problem* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                   const void* v, fa_strides sv, const void* o, fa_strides so, const void* dO,
+                   fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk,
+                   fa_strides sdk, void* dv, fa_strides sdv, float* delta, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

@@ -146,3 +146,87 @@ def test_splitkv_workspace_bytes(lib):
 ])
 def test_splitkv_validation(lib, kw, code):
     assert splitkv(lib, **kw) == code
+
+
+# --------------------------------------------------------------- strided / variable-length
+
+def ex_problem(B=2, H=2, N=16, d=64, cu=None, total=0, causal=0, scale=0.125, dtype=0):
+    return fa.FAProblem(B, H, N, d, cu, total, causal, scale, dtype)
+
+
+def bnhd(H=2, N=16, d=64):
+    return fa.FAStrides(N * H * d, d, H * d)
+
+
+def fwd_ex(lib, p=None, ptrs=None, strides=None, lse=A[4]):
+    vp = ctypes.c_void_p
+    p = ex_problem() if p is None else p
+    q, k, v, o = (A[:4] if ptrs is None else ptrs)
+    sq, sk, sv, so = ([bnhd()] * 4 if strides is None else strides)
+    return lib.fa_forward_ex(ctypes.byref(p), vp(q), sq, vp(k), sk, vp(v), sv, vp(o), so, vp(lse), vp(0))
+
+
+def bwd_ex(lib, p=None, ptrs=None, strides=None):
+    vp = ctypes.c_void_p
+    p = ex_problem() if p is None else p
+    q, k, v, o, do, lse, dq, dk, dv, delta = (A if ptrs is None else ptrs)
+    s = [bnhd()] * 8 if strides is None else strides
+    return lib.fa_backward_ex(ctypes.byref(p), vp(q), s[0], vp(k), s[1], vp(v), s[2], vp(o), s[3], vp(do), s[4],
+                              vp(lse), vp(dq), s[5], vp(dk), s[6], vp(dv), s[7], vp(delta), vp(0))
+
+
+@pytest.mark.parametrize("stride,code", [
+    (fa.FAStrides(2048, 64, 32), fa.FA_ERR_INVALID_ARG),     # row stride below d
+    (fa.FAStrides(2048, 64, 132), fa.FA_ERR_INVALID_ARG),    # not a multiple of 8 elements
+    (fa.FAStrides(2048, -64, 128), fa.FA_ERR_INVALID_ARG),   # negative head stride
+    (fa.FAStrides(-8, 64, 128), fa.FA_ERR_INVALID_ARG),      # negative batch stride
+    (fa.FAStrides(2048, 64, (1 << 23) + 8), fa.FA_ERR_INVALID_ARG),  # row stride above 2^23
+    (fa.FAStrides(1 << 61, 64, 128), fa.FA_ERR_INVALID_ARG),  # extent beyond 2^60 elements
+])
+def test_ex_stride_validation(lib, stride, code):
+    for i in range(4):  # every operand's strides are checked
+        s = [bnhd()] * 4
+        s[i] = stride
+        assert fwd_ex(lib, strides=s) == code, i
+
+
+def test_ex_output_rules(lib):
+    # o aliases q with equal strides: refused (exact element test)
+    assert fwd_ex(lib, ptrs=[A[0], A[1], A[2], A[0]]) == fa.FA_ERR_INVALID_ARG
+    # o interleaved with q inside one (B, N, 2, H, d) buffer shares no element with it, but
+    # with strides differing from q's only the address ranges can be compared: refused
+    s2 = fa.FAStrides(16 * 2 * 2 * 64, 64, 2 * 2 * 64)
+    assert fwd_ex(lib, ptrs=[A[0], A[1], A[2], A[0] + 2 * 64 * 2], strides=[bnhd(), bnhd(), bnhd(), s2]) == \
+        fa.FA_ERR_INVALID_ARG
+    # an output whose heads coincide (head stride 0 with H = 2) is not injective
+    assert fwd_ex(lib, strides=[bnhd()] * 3 + [fa.FAStrides(2048, 0, 128)]) == fa.FA_ERR_INVALID_ARG
+    # lse inside an input
+    assert fwd_ex(lib, lse=A[1] + 64) == fa.FA_ERR_INVALID_ARG
+    # backward: dq and dk the same buffer; delta inside dv
+    p = list(A)
+    p[7] = p[6]
+    assert bwd_ex(lib, ptrs=p) == fa.FA_ERR_INVALID_ARG
+    p = list(A)
+    p[9] = p[8] + 256
+    assert bwd_ex(lib, ptrs=p) == fa.FA_ERR_INVALID_ARG
+    # outputs may not overlap inputs even when inputs overlap each other
+    p = list(A)
+    p[1] = p[2] = p[0]  # q = k = v: allowed for inputs ...
+    p[8] = p[0]         # ... but dv on q is not
+    assert bwd_ex(lib, ptrs=p) == fa.FA_ERR_INVALID_ARG
+
+
+def test_ex_problem_validation(lib):
+    vp = ctypes.c_void_p
+    q, k, v, o = A[:4]
+    s = bnhd()
+    assert lib.fa_forward_ex(None, vp(q), s, vp(k), s, vp(v), s, vp(o), s, vp(A[4]), vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(lib, p=ex_problem(d=96)) == fa.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, p=ex_problem(N=0)) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(lib, p=ex_problem(causal=3)) == fa.FA_ERR_INVALID_ARG
+    # variable lengths: cu_seqlens misaligned, negative total
+    assert fwd_ex(lib, p=ex_problem(cu=A[5] + 4, total=10)) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(lib, p=ex_problem(cu=A[5], total=-1)) == fa.FA_ERR_INVALID_ARG
+    # an empty packed batch validates and enqueues nothing
+    assert fwd_ex(lib, p=ex_problem(cu=A[5], total=0)) == fa.FA_OK
+    assert bwd_ex(lib, p=ex_problem(cu=A[5], total=0)) == fa.FA_OK
