@@ -17,7 +17,9 @@
 namespace {
 
 constexpr double kLog2eD = 1.4426950408889634;
-constexpr long long kMaxRowStride = 1LL << 23;  // copy offsets within a tile stay below 2^32 bytes
+// Row strides up to 2^23 elements keep every source offset inside a 128-row tile below 2^31
+// bytes, under the kernels' out-of-range offset (2^31) used to zero the columns past d.
+constexpr long long kMaxRowStride = 1LL << 23;
 constexpr long long kMaxExtent = 1LL << 60;     // elements an operand may span
 
 using u128 = unsigned __int128;
@@ -49,7 +51,9 @@ int check_shape(const fa_problem& p) {
   if (p.cu_seqlens != nullptr && (p.total < 0 || !aligned16(p.cu_seqlens))) return FA_ERR_INVALID_ARG;
   const long long bh = (long long)p.B * p.H;
   if (bh > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  if (p.d != 64 && p.d != 128) return FA_ERR_UNSUPPORTED;
+  // head dims: multiples of 8 up to 128, run on the 64- or 128-wide kernels with the columns
+  // past d zero on chip
+  if (p.d % 8 != 0 || p.d > 128) return FA_ERR_UNSUPPORTED;
   if (p.N > (1 << 30)) return FA_ERR_UNSUPPORTED;
   // Grids: (N / 64) * B*H tile workgroups, and (statistics rows / 8) * heads row blocks, in
   // one 32-bit grid dimension.
@@ -174,6 +178,7 @@ fa::Geom geom_of(const fa_problem& p) {
   g.N = p.N;
   g.cu = p.cu_seqlens;
   g.T = p.cu_seqlens ? p.total : 0;
+  g.dh = p.d;
   return g;
 }
 
@@ -202,8 +207,14 @@ fa_problem fixed_problem(int B, int H, int N, int d, int causal, float scale, in
 // Most key ranges one Q tile may be cut into.
 constexpr int kMaxSplits = 256;
 
-// Bytes of split-KV workspace: per split and row, d fp32 accumulators, a max and a sum.
-long long splitkv_bytes(long long rows, int d, int splits) { return (long long)splits * rows * (d + 2) * 4; }
+// Width of the kernel that runs head dim d.
+int kernel_d(int d) { return d <= 64 ? 64 : 128; }
+
+// Bytes of split-KV workspace: per split and row, the kernel width's fp32 accumulators, a max
+// and a sum.
+long long splitkv_bytes(long long rows, int d, int splits) {
+  return (long long)splits * rows * (kernel_d(d) + 2) * 4;
+}
 
 int forward_impl(const fa_problem* pp, const void* q, const fa_strides& sq, const void* k, const fa_strides& sk,
                  const void* v, const fa_strides& sv, void* o, const fa_strides& so, float* lse, int splits,

@@ -34,8 +34,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
   const int r = (blockIdx.x - hh * nrb) * RPB + threadIdx.x / TPR;
   // whole rows (TPR consecutive lanes) leave together, so the shuffles below stay in-row
   if (r < stat_rows(geo)) {
-    const u32x4 o = *reinterpret_cast<const u32x4*>(O + stat_row_offset(geo, so, hh, r) + sub * 8);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + stat_row_offset(geo, sdo, hh, r) + sub * 8);
+    // chunks past the operands' head dim count as zero
+    const bool inside = sub * 8 < geo.dh;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 o = inside ? *reinterpret_cast<const u32x4*>(O + stat_row_offset(geo, so, hh, r) + sub * 8) : z;
+    const u32x4 g = inside ? *reinterpret_cast<const u32x4*>(dO + stat_row_offset(geo, sdo, hh, r) + sub * 8) : z;
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -121,8 +124,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
   // Keys past N, and with the causal mask keys after the row, are hidden: key <= key_lim.
   const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 
-  stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, N, rsk, wave);
-  stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, N, rsv, wave);
+  const int dh = geo.dh;
+  stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, N, rsk, dh, wave);
+  stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, N, rsv, dh, wave);
 
   Frag qf[KS], dof[KS];
   float lse2, dl;
@@ -130,8 +134,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     const bool ok = qrow < N;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[ks].v = gload16(Qh + (size_t)qrow * rsq + ks * 16 + h * 8, ok);
-      dof[ks].v = gload16(dOh + (size_t)qrow * rsdo + ks * 16 + h * 8, ok);
+      const bool okc = ok && ks * 16 + h * 8 < dh;
+      qf[ks].v = gload16(Qh + (size_t)qrow * rsq + ks * 16 + h * 8, okc);
+      dof[ks].v = gload16(dOh + (size_t)qrow * rsdo + ks * 16 + h * 8, okc);
     }
     lse2 = ok ? LSE[sq_.stat + qrow] * kLog2e : 0.f;
     dl = ok ? Delta[sq_.stat + qrow] : 0.f;
@@ -175,8 +180,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
     // this lane's row iff key <= key_lim, i.e. iff its compile-time offset is <= thr.
     const int thr = key_lim - t * BN - 4 * h;
     const int tn = min(t + 1, ntiles - 1);
-    const TileSrc rk = tile_src<D, BN>(Kh, tn * BN, N, rsk);
-    const TileSrc rv = tile_src<D, BN>(Vh, tn * BN, N, rsv);
+    const TileSrc rk = tile_src<D, BN>(Kh, tn * BN, N, rsk, dh);
+    const TileSrc rv = tile_src<D, BN>(Vh, tn * BN, N, rsv, dh);
     // fragment i of a K or V tile: key block i % KB (so consecutive MFMAs are independent),
     // k-step i / KB
     auto rfrag = [&](const uint16_t* tile, int i) {
@@ -298,7 +303,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
         u32x2 w;
         w[0] = T::pack2(acc[db][4 * g + 0] * scale, acc[db][4 * g + 1] * scale);
         w[1] = T::pack2(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
-        *reinterpret_cast<u32x2*>(row + db * 32 + 8 * g + 4 * h) = w;
+        // columns db*32 + 8g + 4h .. +3 exist iff db*32 + 8g < dh (dh is a multiple of 8)
+        if (db * 32 + 8 * g < dh) *reinterpret_cast<u32x2*>(row + db * 32 + 8 * g + 4 * h) = w;
       }
   }
   }  // pass
@@ -334,11 +340,11 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
 
 template <typename T>
 static hipError_t pre_dt(const BwdArgs& a) {
-  return a.d == 64 ? launch_pre_t<T, 64>(a) : launch_pre_t<T, 128>(a);
+  return a.d <= 64 ? launch_pre_t<T, 64>(a) : launch_pre_t<T, 128>(a);
 }
 template <typename T>
 static hipError_t dq_dt(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_dq_t<T, 64, true>(a) : launch_dq_t<T, 64, false>(a);
+  if (a.d <= 64) return a.causal ? launch_dq_t<T, 64, true>(a) : launch_dq_t<T, 64, false>(a);
   return a.causal ? launch_dq_t<T, 128, true>(a) : launch_dq_t<T, 128, false>(a);
 }
 

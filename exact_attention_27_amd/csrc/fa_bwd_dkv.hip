@@ -96,17 +96,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   const int it_begin = CAUSAL ? (k0 / BQ) : 0;
   const int it_end = (N + BQ - 1) / BQ;
 
-  stage_rows_swz_buf<D, BK, NW, true>(lds_v, Vh, k0, N, rsv, wave);
-  stage_rows_swz_buf<D, BQ, NW, true>(lds_q0, Qh, it_begin * BQ, N, rsq, wave);
-  stage_rows_swz_buf<D, BQ, NW, true>(lds_do0, dOh, it_begin * BQ, N, rsdo, wave);
-  if (wave == NW - 1) stage_stats_buf(lds_st0, lse_h, dl_h, it_begin * BQ, N);
+  const int dh = geo.dh;
+  stage_rows_swz_buf<D, BK, NW, true>(lds_v, Vh, k0, N, rsv, dh, wave);
+  stage_rows_swz_buf<D, BQ, NW, true>(lds_q0, Qh, it_begin * BQ, N, rsq, dh, wave);
+  stage_rows_swz_buf<D, BQ, NW, true>(lds_do0, dOh, it_begin * BQ, N, rsdo, dh, wave);
+  if (wave == NW - 1) stage_stats_buf((FA_LDS float*)lds_st0, lse_h, dl_h, it_begin * BQ, N);
 
   // Pinned K fragments (B operand of S = Q K^T): lane holds K[key][16ks + 8h .. +7].
   Frag kf[KS];
   {
     const bool ok = key < N;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks].v = gload16(Kh + (size_t)key * rsk + ks * 16 + h * 8, ok);
+    for (int ks = 0; ks < KS; ++ks) kf[ks].v = gload16(Kh + (size_t)key * rsk + ks * 16 + h * 8, ok && ks * 16 + h * 8 < dh);
   }
   f32x16 acc_dk[DB], acc_dv[DB];
 #pragma unroll
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   // (always_inline: six copies of this body exceed the inliner's budget, and a call would
   // leave the accumulators in scratch memory)
   auto step = [&](auto mask_tag, int it, const uint16_t* qs, const uint16_t* dos, const float* st, uint16_t* qn,
-                  uint16_t* don, float* stn) __attribute__((always_inline)) {
+                  uint16_t* don, FA_LDS float* stn) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int qbase = it * BQ;
     // Register i holds query row qbase + 4h + 8(i/4) + (i%4) of this lane's key. It is visible
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
     int vrow = wave * 32 * D * 2;
     asm volatile("" : "+v"(vrow));
     const int itn = min(it + 1, it_end - 1);
-    const TileSrc rq = tile_src<D, BQ>(Qh, itn * BQ, N, rsq);
-    const TileSrc rdo = tile_src<D, BQ>(dOh, itn * BQ, N, rsdo);
+    const TileSrc rq = tile_src<D, BQ>(Qh, itn * BQ, N, rsq, dh);
+    const TileSrc rdo = tile_src<D, BQ>(dOh, itn * BQ, N, rsdo, dh);
     if (wave == NW - 1) stage_stats_buf(stn, lse_h, dl_h, itn * BQ, N);
 
     // this lane's LSE (then D) values for register group g (rows 8g + 4h .. +3), each read
@@ -275,8 +276,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   using F = std::false_type;
   using Tr = std::true_type;
   auto pair = [&](auto mask_tag, int it) __attribute__((always_inline)) {
-    step(mask_tag, it, lds_q0, lds_do0, lds_st0, lds_q1, lds_do1, lds_st1);
-    step(mask_tag, it + 1, lds_q1, lds_do1, lds_st1, lds_q0, lds_do0, lds_st0);
+    step(mask_tag, it, lds_q0, lds_do0, lds_st0, lds_q1, lds_do1, (FA_LDS float*)lds_st1);
+    step(mask_tag, it + 1, lds_q1, lds_do1, lds_st1, lds_q0, lds_do0, (FA_LDS float*)lds_st0);
   };
   const bool key_tail = k0 + BK > N;
   const int plain_begin = key_tail ? it_end : (CAUSAL ? min(it_begin + BK / BQ, it_end) : it_begin);
@@ -300,8 +301,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
         wk[1] = T::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale);
         wv[0] = T::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]);
         wv[1] = T::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3]);
-        *reinterpret_cast<u32x2*>(dk_row + db * 32 + 8 * g + 4 * h) = wk;
-        *reinterpret_cast<u32x2*>(dv_row + db * 32 + 8 * g + 4 * h) = wv;
+        // columns db*32 + 8g + 4h .. +3 exist iff db*32 + 8g < dh (dh is a multiple of 8): a
+        // wave-uniform test
+        if (db * 32 + 8 * g < dh) {
+          *reinterpret_cast<u32x2*>(dk_row + db * 32 + 8 * g + 4 * h) = wk;
+          *reinterpret_cast<u32x2*>(dv_row + db * 32 + 8 * g + 4 * h) = wv;
+        }
       }
   }
   }  // pass
@@ -323,7 +328,7 @@ static hipError_t launch_dkv_t(const BwdArgs& a) {
 
 template <typename T>
 static hipError_t dkv_dt(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_dkv_t<T, 64, true>(a) : launch_dkv_t<T, 64, false>(a);
+  if (a.d <= 64) return a.causal ? launch_dkv_t<T, 64, true>(a) : launch_dkv_t<T, 64, false>(a);
   return a.causal ? launch_dkv_t<T, 128, true>(a) : launch_dkv_t<T, 128, false>(a);
 }
 

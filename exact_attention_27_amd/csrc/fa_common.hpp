@@ -273,20 +273,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 // Source of a ROWS-row tile: one descriptor over rows [grow0, grow0 + ROWS) of a head whose
-// rows are rs elements apart, ending with the last existing row's D elements (empty if none
-// exists), so every row at or past n_rows reads as zero. Wave-uniform.
+// rows are rs elements apart and dh <= D elements wide, ending with the last existing row's
+// dh elements (empty if none exists), so every row at or past n_rows reads as zero.
+// Wave-uniform.
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rsrc;
-  int rs;
+  int rs, dh;
 };
 template <int D, int ROWS>
-__device__ __forceinline__ TileSrc tile_src(const uint16_t* head, int grow0, int n_rows, int rs) {
+__device__ __forceinline__ TileSrc tile_src(const uint16_t* head, int grow0, int n_rows, int rs, int dh) {
   TileSrc t;
   const int avail = __builtin_amdgcn_readfirstlane(max(0, min(n_rows - grow0, ROWS)));
-  t.rsrc = make_rsrc(head + (size_t)grow0 * rs, avail > 0 ? ((avail - 1) * rs + D) * 2 : 0);
+  t.rsrc = make_rsrc(head + (size_t)grow0 * rs, avail > 0 ? ((avail - 1) * rs + dh) * 2 : 0);
   t.rs = rs;
+  t.dh = dh;
   return t;
 }
+// A source offset no descriptor reaches (sizes stay below 2^31): the range check returns
+// zero for it without touching memory.
+constexpr int kOffOutOfRange = (int)0x80000000u;
 // Copy k (0 <= k < ROWS*D*2/1024/NW) of wave `wave`'s share of a ROWS-row tile of D 16-bit
 // elements: 1 KB, i.e. RPI = 1024/(2D) whole rows starting at row ins*RPI, ins = wave + k*NW,
 // landing swizzled at tile[ins * 512 ...]. The per-lane part of the source offset (row within
@@ -307,7 +312,9 @@ __device__ __forceinline__ void stage_copy(uint16_t* tile, const TileSrc& src, i
   const int ins = wave + k * NW;
   const int l = lane_id();
   const int lrow = l / LPR;
-  int lane_ofs = lrow * src.rs * 2 + (((l % LPR) ^ swz<D>(wave * RPI + lrow)) << 4);  // swz(ins*RPI + lrow)
+  const int chunk = (l % LPR) ^ swz<D>(wave * RPI + lrow);  // = swz(ins*RPI + lrow): period 16
+  // columns past the operand's head dim read as zero
+  int lane_ofs = chunk * 8 < src.dh ? lrow * src.rs * 2 + (chunk << 4) : kOffOutOfRange;
   if (SHARED_OFS) asm volatile("" : "+v"(lane_ofs));
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc, (FA_LDS void*)(tile + ins * 512), 16,
                                            lane_ofs + ins * (RPI * 2) * src.rs, 0, 0, 0);
@@ -315,8 +322,8 @@ __device__ __forceinline__ void stage_copy(uint16_t* tile, const TileSrc& src, i
 // All of wave `wave`'s copies of the tile at rows [grow0, grow0 + ROWS).
 template <int D, int ROWS, int NW, bool SHARED_OFS = false>
 __device__ __forceinline__ void stage_rows_swz_buf(uint16_t* tile, const uint16_t* head, int grow0, int n_rows, int rs,
-                                                   int wave) {
-  const TileSrc src = tile_src<D, ROWS>(head, grow0, n_rows, rs);
+                                                   int dh, int wave) {
+  const TileSrc src = tile_src<D, ROWS>(head, grow0, n_rows, rs, dh);
 #pragma unroll
   for (int k = 0; k < ROWS * D * 2 / 1024 / NW; ++k) stage_copy<D, ROWS, NW, SHARED_OFS>(tile, src, wave, k);
 }
@@ -326,7 +333,9 @@ __device__ __forceinline__ void stage_rows_swz_buf(uint16_t* tile, const uint16_
 // Two full-wave copies with one descriptor each: lane-divergent copies from two descriptors
 // get merged by the compiler into one copy with a per-lane descriptor.
 constexpr int kStatB = 64;  // offset of the second array's values in a statistics slot
-__device__ __forceinline__ void stage_stats_buf(float* dst, const float* a, const float* b, int r0, int n_rows) {
+// dst is an LDS pointer already (cast from the __shared__ array itself), so no generic-to-LDS
+// conversion with its null test is left for the compiler to place.
+__device__ __forceinline__ void stage_stats_buf(FA_LDS float* dst, const float* a, const float* b, int r0, int n_rows) {
   const int voff = (lane_id() & 31) * 4;
   const int avail = max(0, min(n_rows - r0, 32));
   __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a + r0, avail * 4), (FA_LDS void*)dst, 4, voff, 0, 0, 0);

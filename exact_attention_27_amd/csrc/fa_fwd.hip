@@ -124,8 +124,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   }
   const int last = t1 - 1;
 
-  auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, N, rsk, wave); };
-  auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, N, rsv, wave); };
+  const int dh = geo.dh;
+  auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, N, rsk, dh, wave); };
+  auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, N, rsv, dh, wave); };
   stage_k(t0, lds_k0);
   stage_v(t0, lds_v0);
   stage_k(min(t0 + 1, last), lds_k1);
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
   {
     const bool ok = qrow < N;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks].v = gload16(Qh + (size_t)qrow * rsq + ks * 16 + h * 8, ok);
+    for (int ks = 0; ks < KS; ++ks) qf[ks].v = gload16(Qh + (size_t)qrow * rsq + ks * 16 + h * 8, ok && ks * 16 + h * 8 < dh);
   }
 
   f32x16 acc[DB];
@@ -281,8 +282,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
     // Copies of K(t+2) and V(t+1): descriptors now, the copies themselves spread over the
     // chunks of [A] (issued all at once, the workgroup's waves queue behind each other in the
     // texture unit right after the barrier).
-    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 2, last) * BN, N, rsk);
-    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, N, rsv);
+    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 2, last) * BN, N, rsk, dh);
+    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, N, rsv, dh);
     constexpr int CPW = BN * D * 2 / 1024 / NW;  // copies per wave per tile
 
     // [A] S(t+1) on the matrix cores while the VALU exponentiates S(t). Written out as 16
@@ -439,7 +440,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
         u32x2 w;
         w[0] = T::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv);
         w[1] = T::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
+        // columns db*32 + 8g + 4h .. +3 exist iff db*32 + 8g < dh (dh is a multiple of 8)
+        if (db * 32 + 8 * g < dh) *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
       }
     if (LSE != nullptr && h == 0) LSE[sq_.stat + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
   }
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   u32x2 w2;
   w2[0] = T::pack2(a0 * inv, a1 * inv);
   w2[1] = T::pack2(a2 * inv, a3 * inv);
-  *reinterpret_cast<u32x2*>(O + stat_row_offset(geo, so, hh, r) + sub * 4) = w2;
+  if (sub * 4 < geo.dh) *reinterpret_cast<u32x2*>(O + stat_row_offset(geo, so, hh, r) + sub * 4) = w2;
   if (sub == 0 && LSE != nullptr) LSE[row] = (Mr + __log2f(L)) * kLn2;
 }
 
@@ -503,8 +505,8 @@ static hipError_t launch_merge_t(const FwdArgs& a) {
 }
 
 static hipError_t launch_merge(const FwdArgs& a) {
-  if (a.bf16) return a.d == 64 ? launch_merge_t<BF16, 64>(a) : launch_merge_t<BF16, 128>(a);
-  return a.d == 64 ? launch_merge_t<FP16, 64>(a) : launch_merge_t<FP16, 128>(a);
+  if (a.bf16) return a.d <= 64 ? launch_merge_t<BF16, 64>(a) : launch_merge_t<BF16, 128>(a);
+  return a.d <= 64 ? launch_merge_t<FP16, 64>(a) : launch_merge_t<FP16, 128>(a);
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -535,7 +537,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
 
 template <typename T>
 static hipError_t launch_fwd_dt(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_fwd_t<T, 64, true>(a) : launch_fwd_t<T, 64, false>(a);
+  if (a.d <= 64) return a.causal ? launch_fwd_t<T, 64, true>(a) : launch_fwd_t<T, 64, false>(a);
   return a.causal ? launch_fwd_t<T, 128, true>(a) : launch_fwd_t<T, 128, false>(a);
 }
 

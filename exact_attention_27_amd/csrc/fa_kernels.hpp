@@ -23,6 +23,8 @@ struct Geom {
   int B, H, N;
   const int* cu;
   int T;
+  int dh;  // head dim of the operands: a multiple of 8, at most the kernel's D; the columns
+           // [dh, D) of every tile are zero on chip and never stored
 };
 
 struct FwdArgs {

@@ -142,6 +142,7 @@ VARLEN_CASES = [
     ((37, 1, 200, 0, 128, 65), 3, 128, FI.FP16, False),
     ((300, 5, 64), 2, 128, FI.BF16, True),
     ((1,), 1, 64, FI.FP16, True),
+    ((37, 1, 130), 2, 96, FI.BF16, True),
 ]
 
 

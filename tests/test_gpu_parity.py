@@ -189,9 +189,10 @@ def test_deterministic(fa):
         assert torch.equal(a, b)
 
 
-def test_unsupported_head_dim_raises(fa):
+@pytest.mark.parametrize("d", [100, 136, 256])
+def test_unsupported_head_dim_raises(fa, d):
     import torch
-    q = torch.zeros(1, 1, 16, 96, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(1, 1, 16, d, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.FAError) as e:
         fa.attention_forward(q, q, q, False)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
