@@ -36,6 +36,8 @@ SOURCES = {
     "fa_fwd.hip": VGPR_FORM,
     "fa_bwd.hip": VGPR_FORM,
     "fa_bwd_dkv.hip": VGPR_FORM,
+    # 256-wide dK/dV: more registers than the VGPR form can hold (see the file's header)
+    "fa_bwd_dkv_wide.hip": [],
 }
 
 

@@ -18,7 +18,8 @@ namespace {
 
 constexpr double kLog2eD = 1.4426950408889634;
 // Row strides up to 2^23 elements keep every source offset inside a 128-row tile below 2^31
-// bytes, under the kernels' out-of-range offset (2^31) used to zero the columns past d.
+// bytes, under the kernels' out-of-range offset (2^31) used to zero the columns past d. (The
+// 256-wide kernels stage tiles of at most 128 rows too.)
 constexpr long long kMaxRowStride = 1LL << 23;
 constexpr long long kMaxExtent = 1LL << 60;     // elements an operand may span
 
@@ -51,15 +52,15 @@ int check_shape(const fa_problem& p) {
   if (p.cu_seqlens != nullptr && (p.total < 0 || !aligned16(p.cu_seqlens))) return FA_ERR_INVALID_ARG;
   const long long bh = (long long)p.B * p.H;
   if (bh > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  // head dims: multiples of 8 up to 128, run on the 64- or 128-wide kernels with the columns
-  // past d zero on chip
-  if (p.d % 8 != 0 || p.d > 128) return FA_ERR_UNSUPPORTED;
+  // head dims: multiples of 8 up to 256, run on the 64-, 128- or 256-wide kernels with the
+  // columns past d zero on chip
+  if (p.d % 8 != 0 || p.d > 256) return FA_ERR_UNSUPPORTED;
   if (p.N > (1 << 30)) return FA_ERR_UNSUPPORTED;
-  // Grids: (N / 64) * B*H tile workgroups, and (statistics rows / 8) * heads row blocks, in
+  // Grids: (N / 64) * B*H tile workgroups, and (statistics rows / 4) * heads row blocks, in
   // one 32-bit grid dimension.
   if (((long long)p.N + 63) / 64 * bh > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   const long long stat = p.cu_seqlens ? (long long)p.H * p.total : bh * p.N;
-  if (stat / 8 + bh > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (stat / 4 + bh > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -208,7 +209,7 @@ fa_problem fixed_problem(int B, int H, int N, int d, int causal, float scale, in
 constexpr int kMaxSplits = 256;
 
 // Width of the kernel that runs head dim d.
-int kernel_d(int d) { return d <= 64 ? 64 : 128; }
+int kernel_d(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
 
 // Bytes of split-KV workspace: per split and row, the kernel width's fp32 accumulators, a max
 // and a sum.

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
 //   [dQ] dQ^T += K^T dS^T     || dS = P (dP - D) of the next 16-key group
 // Steps on the causal diagonal or the key tail run a copy of the body with the mask.
 template <typename T, int D, int BN, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, Geom geo, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdq,
@@ -340,12 +340,13 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
 
 template <typename T>
 static hipError_t pre_dt(const BwdArgs& a) {
-  return a.d <= 64 ? launch_pre_t<T, 64>(a) : launch_pre_t<T, 128>(a);
+  return a.d <= 64 ? launch_pre_t<T, 64>(a) : a.d <= 128 ? launch_pre_t<T, 128>(a) : launch_pre_t<T, 256>(a);
 }
 template <typename T>
 static hipError_t dq_dt(const BwdArgs& a) {
   if (a.d <= 64) return a.causal ? launch_dq_t<T, 64, true>(a) : launch_dq_t<T, 64, false>(a);
-  return a.causal ? launch_dq_t<T, 128, true>(a) : launch_dq_t<T, 128, false>(a);
+  if (a.d <= 128) return a.causal ? launch_dq_t<T, 128, true>(a) : launch_dq_t<T, 128, false>(a);
+  return a.causal ? launch_dq_t<T, 256, true>(a) : launch_dq_t<T, 256, false>(a);
 }
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a) { return a.bf16 ? pre_dt<BF16>(a) : pre_dt<FP16>(a); }

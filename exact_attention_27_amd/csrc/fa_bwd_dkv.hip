@@ -30,7 +30,7 @@ namespace fa {
 // straight from global memory (no staging registers). Two workgroups fit a CU, so two waves
 // share each SIMD and hide each other's latencies.
 template <typename T, int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
+__global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, Geom geo, Strides sq, Strides sk, Strides sv,
@@ -97,9 +97,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
   const int it_end = (N + BQ - 1) / BQ;
 
   const int dh = geo.dh;
-  stage_rows_swz_buf<D, BK, NW, true>(lds_v, Vh, k0, N, rsv, dh, wave);
-  stage_rows_swz_buf<D, BQ, NW, true>(lds_q0, Qh, it_begin * BQ, N, rsq, dh, wave);
-  stage_rows_swz_buf<D, BQ, NW, true>(lds_do0, dOh, it_begin * BQ, N, rsdo, dh, wave);
+  // At two waves per SIMD registers are short: one lane offset serves all of a wave's copies.
+  constexpr bool SHARE = D <= 128;
+  stage_rows_swz_buf<D, BK, NW, SHARE>(lds_v, Vh, k0, N, rsv, dh, wave);
+  stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_q0, Qh, it_begin * BQ, N, rsq, dh, wave);
+  stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_do0, dOh, it_begin * BQ, N, rsdo, dh, wave);
   if (wave == NW - 1) stage_stats_buf((FA_LDS float*)lds_st0, lse_h, dl_h, it_begin * BQ, N);
 
   // Pinned K fragments (B operand of S = Q K^T): lane holds K[key][16ks + 8h .. +7].
@@ -182,9 +184,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(
         if (ks % GAP == 0) {
           const int c = ks / GAP;
           if (c < CPW)
-            stage_copy<D, BQ, NW, true>(qn, rq, wave, c);
+            stage_copy<D, BQ, NW, SHARE>(qn, rq, wave, c);
           else
-            stage_copy<D, BQ, NW, true>(don, rdo, wave, c - CPW);
+            stage_copy<D, BQ, NW, SHARE>(don, rdo, wave, c - CPW);
         }
         if (ks + 2 < KS) qfr[(ks + 2) % 3] = lds_read_rows(qs, rofs[ks + 2]);
         __builtin_amdgcn_sched_barrier(0);
@@ -326,12 +328,21 @@ static hipError_t launch_dkv_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+#ifndef FA_DKV_WIDE_UNIT
 template <typename T>
 static hipError_t dkv_dt(const BwdArgs& a) {
   if (a.d <= 64) return a.causal ? launch_dkv_t<T, 64, true>(a) : launch_dkv_t<T, 64, false>(a);
-  return a.causal ? launch_dkv_t<T, 128, true>(a) : launch_dkv_t<T, 128, false>(a);
+  if (a.d <= 128) return a.causal ? launch_dkv_t<T, 128, true>(a) : launch_dkv_t<T, 128, false>(a);
+  return launch_bwd_dkv_wide(a);
 }
 
 hipError_t launch_bwd_dkv(const BwdArgs& a) { return a.bf16 ? dkv_dt<BF16>(a) : dkv_dt<FP16>(a); }
+#else
+// The 256-wide instances (head dims above 128), built in their own unit (fa_bwd_dkv_wide.hip).
+hipError_t launch_bwd_dkv_wide(const BwdArgs& a) {
+  if (a.bf16) return a.causal ? launch_dkv_t<BF16, 256, true>(a) : launch_dkv_t<BF16, 256, false>(a);
+  return a.causal ? launch_dkv_t<FP16, 256, true>(a) : launch_dkv_t<FP16, 256, false>(a);
+}
+#endif
 
 }  // namespace fa

@@ -135,8 +135,11 @@ __device__ __forceinline__ Frag lds_frag_cols(const uint16_t* base, int stride, 
 //   D = 64  (8 chunks, two rows per bank line): swz(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  static_assert(D == 64 || D == 128, "swizzle defined for head dims 64 and 128");
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  static_assert(D == 64 || D == 128 || D == 256, "swizzle defined for tile widths 64, 128 and 256");
+  // 256 wide (32 chunks, 512-byte rows): the 128-wide permutation on the low 4 chunk bits;
+  // rows are a whole number of bank lines apart in both, so the bank pattern of every read
+  // is the same as at 128
+  return D >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Element offset of (row, col) in a swizzled tile.
@@ -308,11 +311,13 @@ __device__ __forceinline__ void stage_copy(uint16_t* tile, const TileSrc& src, i
   constexpr int RPI = 1024 / ROW_BYTES;  // rows per copy
   constexpr int LPR = ROW_BYTES / 16;    // lanes per row
   static_assert((ROWS * ROW_BYTES / 1024) % NW == 0, "tile copies must split evenly over the waves");
-  static_assert((NW * RPI) % 16 == 0, "a wave's copies must sit whole swizzle periods (16 rows) apart");
+  constexpr bool PERIODIC = (NW * RPI) % 16 == 0;  // a wave's copies sit whole swizzle periods apart
+  static_assert(PERIODIC || !SHARED_OFS, "a shared lane offset needs copies whole swizzle periods apart");
   const int ins = wave + k * NW;
   const int l = lane_id();
   const int lrow = l / LPR;
-  const int chunk = (l % LPR) ^ swz<D>(wave * RPI + lrow);  // = swz(ins*RPI + lrow): period 16
+  // = swz(ins*RPI + lrow) when PERIODIC (period 16)
+  const int chunk = (l % LPR) ^ swz<D>((PERIODIC ? wave : ins) * RPI + lrow);
   // columns past the operand's head dim read as zero
   int lane_ofs = chunk * 8 < src.dh ? lrow * src.rs * 2 + (chunk << 4) : kOffOutOfRange;
   if (SHARED_OFS) asm volatile("" : "+v"(lane_ofs));

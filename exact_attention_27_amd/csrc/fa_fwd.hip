@@ -47,7 +47,7 @@ constexpr float kTau = 8.0f;
 // [splits][BH*N][D] accumulators, then [splits][BH*N] maxima, then [splits][BH*N] sums;
 // merge_kernel combines them.
 template <typename T, int D, int BN, int NW, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
+__global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, Geom geo, Strides sq, Strides sk, Strides sv, Strides so,
     int n_qtiles_max, float c_log2, float* __restrict__ part, long long rows_all, int splits) {
@@ -350,12 +350,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(
         const int g = j / DB, db = j % DB;
         acc[db] = T::mfma(vf[j % 3], pf[g], acc[db]);
         if (g + 1 < NG) {
-          // the next group's 4 packed pairs, 4 / DB of them per chunk
+          // the next group's 4 packed pairs, PPC of them per chunk (the first 4 chunks of the
+          // group when it has more than 4)
           const int gn = g + 1;
+          constexpr int PPC = DB >= 4 ? 1 : 4 / DB;
 #pragma unroll
-          for (int c = 0; c < 4 / DB; ++c) {
-            const int w = db * (4 / DB) + c;
-            pf[gn].v[w] = T::pack2(s[gn / 2][8 * (gn % 2) + 2 * w], s[gn / 2][8 * (gn % 2) + 2 * w + 1]);
+          for (int c = 0; c < PPC; ++c) {
+            const int w = db * PPC + c;
+            if (w < 4) pf[gn].v[w] = T::pack2(s[gn / 2][8 * (gn % 2) + 2 * w], s[gn / 2][8 * (gn % 2) + 2 * w + 1]);
           }
         }
 #pragma unroll
@@ -505,8 +507,9 @@ static hipError_t launch_merge_t(const FwdArgs& a) {
 }
 
 static hipError_t launch_merge(const FwdArgs& a) {
-  if (a.bf16) return a.d <= 64 ? launch_merge_t<BF16, 64>(a) : launch_merge_t<BF16, 128>(a);
-  return a.d <= 64 ? launch_merge_t<FP16, 64>(a) : launch_merge_t<FP16, 128>(a);
+  if (a.bf16)
+    return a.d <= 64 ? launch_merge_t<BF16, 64>(a) : a.d <= 128 ? launch_merge_t<BF16, 128>(a) : launch_merge_t<BF16, 256>(a);
+  return a.d <= 64 ? launch_merge_t<FP16, 64>(a) : a.d <= 128 ? launch_merge_t<FP16, 128>(a) : launch_merge_t<FP16, 256>(a);
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -538,7 +541,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
 template <typename T>
 static hipError_t launch_fwd_dt(const FwdArgs& a) {
   if (a.d <= 64) return a.causal ? launch_fwd_t<T, 64, true>(a) : launch_fwd_t<T, 64, false>(a);
-  return a.causal ? launch_fwd_t<T, 128, true>(a) : launch_fwd_t<T, 128, false>(a);
+  if (a.d <= 128) return a.causal ? launch_fwd_t<T, 128, true>(a) : launch_fwd_t<T, 128, false>(a);
+  return a.causal ? launch_fwd_t<T, 256, true>(a) : launch_fwd_t<T, 256, false>(a);
 }
 
 hipError_t launch_forward(const FwdArgs& a) {

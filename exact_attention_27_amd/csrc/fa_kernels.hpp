@@ -66,6 +66,7 @@ struct BwdArgs {
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_dkv(const BwdArgs& a);
+hipError_t launch_bwd_dkv_wide(const BwdArgs& a);  // head dims above 128 (its own unit)
 hipError_t launch_bwd_dq(const BwdArgs& a);
 
 }  // namespace fa

@@ -26,13 +26,13 @@
  *   Types      dtype FA_FP16 (IEEE binary16) or FA_BF16 (bfloat16). Arithmetic is
  *              fp32 inside (fp32 accumulation on the matrix cores); every fp32 ->
  *              16-bit conversion rounds to nearest even.
- *   Shapes     B, H, N >= 1; head dim d a multiple of 8 up to 128 (d <= 64 runs on the
- *              64-wide kernels, larger d on the 128-wide ones, with the columns past d
- *              zero on chip: exact, at the cost of the padded products). Any N is
- *              accepted (tails are masked). Other head dims (above 128, or not a multiple
- *              of 8) return FA_ERR_UNSUPPORTED -- never a slower or approximate fallback;
- *              the pages note that flash kernels cap the head dim ("FlashAttentionを1から",
- *              section "現場ではこう使う").
+ *   Shapes     B, H, N >= 1; head dim d a multiple of 8 up to 256 (d <= 64 runs on the
+ *              64-wide kernels, d <= 128 on the 128-wide ones, larger d on the 256-wide
+ *              ones, with the columns past d zero on chip: exact, at the cost of the
+ *              padded products). Any N is accepted (tails are masked). Other head dims
+ *              (above 256, or not a multiple of 8) return FA_ERR_UNSUPPORTED -- never a
+ *              slower or approximate fallback; the pages note that flash kernels cap the
+ *              head dim ("FlashAttentionを1から", section "現場ではこう使う").
  *   Mask       causal = 0 (none) or 1: key j is visible to query i iff j <= i
  *              ("Triton 05", section "Causal Masking"; Nq = Nk so top-left and
  *              bottom-right alignment coincide).
@@ -49,7 +49,7 @@
  *              non-positive sizes, 64-bit size overflow, unknown dtype, a causal
  *              flag other than 0/1, or a non-finite / non-positive scale;
  *              FA_ERR_UNSUPPORTED for a valid request this build does not implement
- *              (head dim above 128 or not a multiple of 8); FA_ERR_HIP if a kernel launch reports an
+ *              (head dim above 256 or not a multiple of 8); FA_ERR_HIP if a kernel launch reports an
  *              error. Faults during execution surface at the caller's next
  *              synchronisation, as usual for HIP.
  */
@@ -109,7 +109,7 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
 
 /*
  * Workspace bytes fa_forward_splitkv needs: num_splits * B*H*N * (w + 2) * 4, where w = 64
- * for d <= 64 and 128 otherwise (the width of the kernel that runs d). Returns 0 for
+ * for d <= 64, 128 for d <= 128 and 256 above (the width of the kernel that runs d). Returns 0 for
  * arguments fa_forward_splitkv would refuse (sizes, head dim, num_splits).
  */
 size_t fa_forward_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);

@@ -63,8 +63,9 @@ def bwd(lib, ptrs=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0):
     (dict(lse=A[0] + 16), fa.FA_ERR_INVALID_ARG),        # lse inside q
     (dict(B=1 << 20, H=1 << 20, N=1 << 20, d=64), fa.FA_ERR_INVALID_ARG),  # size overflow
     (dict(d=100), fa.FA_ERR_UNSUPPORTED),   # not a multiple of 8
-    (dict(d=136), fa.FA_ERR_UNSUPPORTED),   # above 128
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=132), fa.FA_ERR_UNSUPPORTED),   # not a multiple of 8
+    (dict(d=264), fa.FA_ERR_UNSUPPORTED),   # above 256
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_forward_validation(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -73,7 +74,7 @@ def test_forward_validation(lib, kw, code):
 def test_backward_validation(lib):
     assert bwd(lib, N=0) == fa.FA_ERR_INVALID_ARG
     assert bwd(lib, d=84) == fa.FA_ERR_UNSUPPORTED
-    assert bwd(lib, d=192) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lib, d=320) == fa.FA_ERR_UNSUPPORTED
     assert bwd(lib, scale=math.nan) == fa.FA_ERR_INVALID_ARG
     assert bwd(lib, causal=-1) == fa.FA_ERR_INVALID_ARG
     assert bwd(lib, dtype=7) == fa.FA_ERR_INVALID_ARG
@@ -131,7 +132,9 @@ def test_splitkv_workspace_bytes(lib):
     assert size(1, 1, 16, 64, 257) == 0
     assert size(1, 1, 16, 96, 2) == 2 * 16 * (128 + 2) * 4   # d = 96 runs 128 wide
     assert size(1, 1, 16, 32, 2) == 2 * 16 * (64 + 2) * 4    # d = 32 runs 64 wide
+    assert size(1, 1, 16, 200, 2) == 2 * 16 * (256 + 2) * 4  # d = 200 runs 256 wide
     assert size(1, 1, 16, 100, 2) == 0          # unsupported head dim
+    assert size(1, 1, 16, 264, 2) == 0
     assert size(0, 1, 16, 64, 2) == 0
 
 
@@ -144,7 +147,7 @@ def test_splitkv_workspace_bytes(lib):
     (dict(ws=A[0] + 64), fa.FA_ERR_INVALID_ARG),                  # workspace inside q
     (dict(ws=A[4]), fa.FA_ERR_INVALID_ARG),                       # workspace aliases lse
     (dict(o=A[1]), fa.FA_ERR_INVALID_ARG),                        # output aliases an input
-    (dict(d=200), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=260), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=math.nan), fa.FA_ERR_INVALID_ARG),
 ])
 def test_splitkv_validation(lib, kw, code):
@@ -224,7 +227,7 @@ def test_ex_problem_validation(lib):
     q, k, v, o = A[:4]
     s = bnhd()
     assert lib.fa_forward_ex(None, vp(q), s, vp(k), s, vp(v), s, vp(o), s, vp(A[4]), vp(0)) == fa.FA_ERR_INVALID_ARG
-    assert fwd_ex(lib, p=ex_problem(d=132)) == fa.FA_ERR_UNSUPPORTED  # above 128
+    assert fwd_ex(lib, p=ex_problem(d=272)) == fa.FA_ERR_UNSUPPORTED  # above 256
     assert fwd_ex(lib, p=ex_problem(d=60)) == fa.FA_ERR_UNSUPPORTED   # not a multiple of 8
     assert fwd_ex(lib, p=ex_problem(N=0)) == fa.FA_ERR_INVALID_ARG
     assert fwd_ex(lib, p=ex_problem(causal=3)) == fa.FA_ERR_INVALID_ARG

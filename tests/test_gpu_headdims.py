@@ -1,6 +1,6 @@
-"""GPU: head dims other than 64 and 128 (multiples of 8 up to 128).
+"""GPU: head dims other than 64 and 128 (multiples of 8 up to 256).
 
-Such a head dim runs on the 64- or 128-wide kernels with the columns past d zero on chip
+Such a head dim runs on the 64-, 128- or 256-wide kernels with the columns past d zero on chip
 (loads past d read zero, stores past d are skipped), which leaves every dot product
 unchanged. Checked here:
   * parity with the fp64 oracle on every head, forward and backward, to the tolerances of
@@ -40,6 +40,10 @@ CASES = [
     (96, 333, FI.BF16, True),
     (96, 64, FI.FP16, False),
     (120, 150, FI.BF16, True),
+    (136, 100, FI.FP16, True),
+    (192, 257, FI.BF16, False),
+    (256, 300, FI.BF16, True),
+    (256, 129, FI.FP16, False),
 ]
 
 
@@ -92,7 +96,7 @@ def test_nothing_written_past_head_dim(fa):
     assert gate <= 1e-2 and float(np.abs(lse[1, 1].cpu().numpy() - lse_ref).max()) <= 1e-3
 
 
-@pytest.mark.parametrize("d,splits", [(40, 3), (96, 2)])
+@pytest.mark.parametrize("d,splits", [(40, 3), (96, 2), (256, 2)])
 def test_head_dim_splitkv(fa, d, splits):
     import torch
     B, H, N, dtype, causal = 1, 2, 300, FI.BF16, True
@@ -102,7 +106,7 @@ def test_head_dim_splitkv(fa, d, splits):
     o = torch.full_like(q, float("nan"))
     lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device)
     nbytes = fa.fa_forward_splitkv_workspace_bytes(B, H, N, d, splits)
-    assert nbytes == splits * B * H * N * ((64 if d <= 64 else 128) + 2) * 4
+    assert nbytes == splits * B * H * N * ((64 if d <= 64 else 128 if d <= 128 else 256) + 2) * 4
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=q.device)
     fa.fa_forward_splitkv(q, k, v, o, lse, causal, scale, splits, ws)
     torch.cuda.synchronize()

@@ -143,6 +143,7 @@ VARLEN_CASES = [
     ((300, 5, 64), 2, 128, FI.BF16, True),
     ((1,), 1, 64, FI.FP16, True),
     ((37, 1, 130), 2, 96, FI.BF16, True),
+    ((70, 200), 2, 256, FI.FP16, True),
 ]
 
 

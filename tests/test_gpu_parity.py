@@ -189,7 +189,7 @@ def test_deterministic(fa):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("d", [100, 136, 256])
+@pytest.mark.parametrize("d", [100, 264, 512])
 def test_unsupported_head_dim_raises(fa, d):
     import torch
     q = torch.zeros(1, 1, 16, d, dtype=torch.bfloat16, device="cuda")
