@@ -56,18 +56,25 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     report, other, objs = [], [], []
+    # one compiler process per unit, all at once (at most len(SOURCES), a handful)
+    procs = []
     for src, extra in SOURCES.items():
         obj = os.path.join(objdir, src + ".o")
         cmd = _common(cc) + extra + ["-Rpass-analysis=kernel-resource-usage", "-c",
                                       os.path.join(CSRC, src), "-o", obj]
-        proc = subprocess.run(cmd, capture_output=True, text=True)
-        report += [ln for ln in proc.stderr.splitlines() if "remark:" in ln]
-        other += [ln for ln in proc.stderr.splitlines()
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    failed = None
+    for src, obj, proc in procs:
+        _, err = proc.communicate()
+        report += [ln for ln in err.splitlines() if "remark:" in ln]
+        other += [ln for ln in err.splitlines()
                   if "remark:" not in ln and "packed-fp32-ops" not in ln and ln.strip()]
-        if proc.returncode != 0:
-            sys.stderr.write("\n".join(other) + "\n")
-            raise RuntimeError(f"hipcc failed on {src} with exit code {proc.returncode}")
+        if proc.returncode != 0 and failed is None:
+            failed = (src, proc.returncode)
         objs.append(obj)
+    if failed is not None:
+        sys.stderr.write("\n".join(other) + "\n")
+        raise RuntimeError(f"hipcc failed on {failed[0]} with exit code {failed[1]}")
     link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
     proc = subprocess.run(link, capture_output=True, text=True)
     if proc.returncode != 0:
