@@ -152,6 +152,95 @@ def sweep_configs(fa, FI, torch, np, dev, log):
     return out
 
 
+def _time11(fn, torch, np, stream):
+    """11 runs of fn bracketed by HIP events on `stream`, the first discarded (microseconds)."""
+    ts = []
+    for _ in range(11):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts = np.array(ts[1:]) * 1e3
+    return {"mean_us": float(ts.mean()), "std_us": float(ts.std()), "median_us": float(np.median(ts))}
+
+
+def sweep_extras(fa, FI, torch, np, dev, log):
+    """The strided, variable-length and other-head-dim entry points on LLM-layer-sized work:
+    forward and backward, each timed as 11 runs (first discarded); FLOPs counted on the work
+    the problem defines (for a packed batch, each sequence's own causal triangle)."""
+    out = []
+    stream = torch.cuda.current_stream(dev)
+    H, N, d = 32, 4096, 128
+
+    def rec(label, F, fwd, bwd):
+        r = {"extra": label, "fwd": fwd, "bwd": bwd, "counted_flop": F,
+             "fwd_tflops": F / (fwd["mean_us"] * 1e-6) / 1e12,
+             "fwd_bwd_tflops": 3.5 * F / ((fwd["mean_us"] + bwd["mean_us"]) * 1e-6) / 1e12}
+        log(f"  {label:58s} fwd {fwd['mean_us']:9.1f} us  bwd {bwd['mean_us']:9.1f} us  "
+            f"fwd {r['fwd_tflops']:7.1f}  fwd+bwd {r['fwd_bwd_tflops']:7.1f} TFLOP/s")
+        out.append(r)
+
+    def tensors(shape, dtype, seed):
+        bits = FI.draw_bits(shape, dtype, seed)
+        tdt = torch.bfloat16 if dtype == FI.BF16 else torch.float16
+        return [torch.from_numpy(bits[n].view(np.int16)).to(dev).view(tdt) for n in FI.TENSOR_ORDER]
+
+    # (B, N, H, d) storage at the headline shape, through fa_forward_ex / fa_backward_ex
+    q, k, v, do = (t.transpose(1, 2).contiguous() for t in tensors((4, H, N, d), FI.BF16, 1004))
+    o = torch.empty_like(q)
+    lse = torch.empty(4, H, N, dtype=torch.float32, device=dev)
+    delta, dq, dk, dv = torch.empty_like(lse), torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    F = 4.0 * 4 * H * N * N * d * 0.5
+    rec("B=4 H=32 N=4096 d=128 causal bf16, (B,N,H,d) strided", F,
+        _time11(lambda: fa.fa_forward_ex(q, k, v, o, lse, True, d ** -0.5, "bnhd", stream=stream), torch, np, stream),
+        _time11(lambda: fa.fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, True, d ** -0.5, "bnhd",
+                                          stream=stream), torch, np, stream))
+    del q, k, v, do, o, lse, delta, dq, dk, dv
+
+    # a packed batch of 8 sequences with a seeded length mix, and the same batch padded to
+    # its longest sequence (what the variable-length interface saves)
+    lengths = FI.varlen_lengths(8, N, 3001)
+    T = int(lengths.sum())
+    q, k, v, do = (t[0].transpose(0, 1).contiguous() for t in tensors((1, H, T, d), FI.BF16, 3002))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(H, T, dtype=torch.float32, device=dev)
+    delta, dq, dk, dv = torch.empty_like(lse), torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    F = float(sum(4.0 * H * n * n * d * 0.5 for n in lengths))
+    rec(f"varlen 8 seqs, {T} tokens (max {N}) H=32 d=128 causal bf16", F,
+        _time11(lambda: fa.fa_forward_ex(q, k, v, o, lse, True, d ** -0.5, cu_seqlens=cu, max_seqlen=N,
+                                         stream=stream), torch, np, stream),
+        _time11(lambda: fa.fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, True, d ** -0.5, cu_seqlens=cu,
+                                          max_seqlen=N, stream=stream), torch, np, stream))
+    del q, k, v, do, o, lse, delta, dq, dk, dv
+    q, k, v, do = tensors((8, H, N, d), FI.BF16, 3003)
+    o = torch.empty_like(q)
+    lse = torch.empty(8, H, N, dtype=torch.float32, device=dev)
+    delta, dq, dk, dv = torch.empty_like(lse), torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    rec(f"same batch padded to 8 x {N} (useful work counted)", F,
+        _time11(lambda: fa.fa_forward(q, k, v, o, lse, True, d ** -0.5, stream), torch, np, stream),
+        _time11(lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, True, d ** -0.5, stream), torch, np,
+                stream))
+    del q, k, v, do, o, lse, delta, dq, dk, dv
+
+    # other head dims at B=4 H=32 N=4096 causal (d = 96 runs 128 wide, 256 at one wave per SIMD)
+    for dd, hh in ((96, 32), (256, 16)):
+        q, k, v, do = tensors((4, hh, N, dd), FI.BF16, 3100 + dd)
+        o = torch.empty_like(q)
+        lse = torch.empty(4, hh, N, dtype=torch.float32, device=dev)
+        delta, dq, dk, dv = torch.empty_like(lse), torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        F = 4.0 * 4 * hh * N * N * dd * 0.5
+        rec(f"B=4 H={hh} N=4096 d={dd} causal bf16", F,
+            _time11(lambda: fa.fa_forward(q, k, v, o, lse, True, dd ** -0.5, stream), torch, np, stream),
+            _time11(lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, True, dd ** -0.5, stream), torch,
+                    np, stream))
+        del q, k, v, do, o, lse, delta, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +377,8 @@ def main():
     if args.sweep:
         log("sweep over the workloads (11 runs each, first discarded):")
         sweep = sweep_configs(fa, FI, torch, np, dev, log)
+        log("strided, variable-length and other head dims (11 runs each, first discarded):")
+        sweep += sweep_extras(fa, FI, torch, np, dev, log)
 
     cpu = None
     if not args.no_cpu_baseline:

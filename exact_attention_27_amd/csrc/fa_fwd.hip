@@ -168,15 +168,15 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   }
   // K fragment i = (key block i / KS, k-step i % KS); V^T fragment (d block db, keys of the
   // 16-key group g).
-  auto kfrag = [&](const uint16_t* ktile, int i) {
+  auto kfrag = [&](const uint16_t* ktile, int i) __attribute__((always_inline)) {
     return lds_read_rows(ktile, kofs[i % KS] + (i / KS) * 32 * D * 2);
   };
-  auto vfrag = [&](const uint16_t* vtile, int db, int g) {
+  auto vfrag = [&](const uint16_t* vtile, int db, int g) __attribute__((always_inline)) {
     return lds_read_cols(vtile, vofs[db][0] + g * 16 * D * 2, vofs[db][1] + (g * 16 + 8) * D * 2);
   };
 
   // S^T tile (32 keys x 32 rows per block) from a K slot.
-  auto qk = [&](const uint16_t* ktile, f32x16 (&s)[KB]) {
+  auto qk = [&](const uint16_t* ktile, f32x16 (&s)[KB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = T::mfma(kfrag(ktile, kb * KS), qf[0], f32x16{});
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   auto masked = [](float x, int kb, int i, int thr) {
     return (kb * 32 + 8 * (i >> 2) + (i & 3)) > thr ? -INFINITY : x;
   };
-  auto mask = [&](f32x16 (&s)[KB], int t) {
+  auto mask = [&](f32x16 (&s)[KB], int t) __attribute__((always_inline)) {
     const int thr = mask_thr(t);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   // exceeds the reference by more than kTau; otherwise p = 2^(c s - m_ref) <= 2^kTau
   // accumulates against the old one. O = acc / l and LSE = ln2 (m_ref + log2 l) hold for any
   // reference that acc and l share, so skipping a move only skips a rescale of acc.
-  auto update_ref = [&](float mx) {
+  auto update_ref = [&](float mx) __attribute__((always_inline)) {
     mx = half_swap_max(mx) * c_log2;
     moved = mx > m_run + kTau;
     m_run = moved ? mx : m_run;
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     alpha = __builtin_amdgcn_exp2f(m_ref - ref);  // 1 if kept; finite in every case
     m_ref = ref;
   };
-  auto row_max = [&](const f32x16 (&s)[KB]) {
+  auto row_max = [&](const f32x16 (&s)[KB]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     update_ref(mx);
   };
   // P = 2^(c s - m_ref) packed to 16-bit B operands; l = alpha l + row sum.
-  auto softmax_p = [&](f32x16 (&s)[KB], Frag (&pf)[KB][2]) {
+  auto softmax_p = [&](f32x16 (&s)[KB], Frag (&pf)[KB][2]) __attribute__((always_inline)) {
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   };
   // The rescale is owed by the whole wave when any lane's reference moved (alpha = 1 for the
   // others); the branch is wave-uniform and rarely taken.
-  auto rescale = [&]() {
+  auto rescale = [&]() __attribute__((always_inline)) {
     if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
     }
   };
-  auto pv = [&](const uint16_t* vtile, const Frag (&pf)[KB][2]) {
+  auto pv = [&](const uint16_t* vtile, const Frag (&pf)[KB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < KB * 2; ++g)
 #pragma unroll
@@ -272,7 +272,9 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   ring_barrier();
 
   // ---- steps t = t0 .. last-1, slot parity P = (t - t0) & 1 fixed at compile time.
-  auto step = [&](auto mask_tag, auto parity_tag, int t) {
+  // (always_inline throughout: at the 256-wide tile these bodies exceed the inliner's budget,
+  // and a call would leave the accumulators in scratch memory)
+  auto step = [&](auto mask_tag, auto parity_tag, int t) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(parity_tag)::value;
     const uint16_t* kcur = P ? lds_k0 : lds_k1;  // K(t+1)
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     {
       constexpr int NA = KB * KS;  // MFMAs in this half
       Frag kf[3];
-      auto kread = [&](int i) { return kfrag(kcur, (i % KB) * KS + i / KB); };
+      auto kread = [&](int i) __attribute__((always_inline)) { return kfrag(kcur, (i % KB) * KS + i / KB); };
       kf[0] = kread(0);
       kf[1] = kread(1);
       constexpr int GAP = NA / (2 * CPW);  // chunks between two copies
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
       Frag pf[NG];
       pf[0] = pack_group<T>(s[0], 0);
       Frag vf[3];
-      auto vread = [&](int j) { return vfrag(vcur, j % DB, j / DB); };
+      auto vread = [&](int j) __attribute__((always_inline)) { return vfrag(vcur, j % DB, j / DB); };
       vf[0] = vread(0);
       vf[1] = vread(1);
       float mx = -INFINITY, rs = 0.f;
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
   };
   // ---- last tile: P and P V only.
-  auto drain = [&](auto parity_tag) {
+  auto drain = [&](auto parity_tag) __attribute__((always_inline)) {
     constexpr int P = decltype(parity_tag)::value;
     Frag pf[KB][2];
     softmax_p(s, pf);

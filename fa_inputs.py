@@ -164,3 +164,13 @@ def edge_shapes() -> Iterator[tuple]:
                 for causal in (False, True):
                     seed += 1
                     yield (1, 2, N, d, dtype, causal, seed)
+
+
+def varlen_lengths(n_seq: int, n_max: int, seed: int) -> np.ndarray:
+    """A seeded mix of sequence lengths for variable-length batches: n_seq lengths drawn
+    uniformly from [n_max // 8, n_max] (numpy PCG64), the last forced to n_max so the
+    longest sequence is always present. Returns int64 lengths."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = rng.integers(max(1, n_max // 8), n_max + 1, size=n_seq)
+    lengths[-1] = n_max
+    return lengths.astype(np.int64)
