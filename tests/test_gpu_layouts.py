@@ -272,3 +272,35 @@ def test_flash_attn_varlen_func_autograd(fa):
     assert torch.equal(o.detach().view(torch.int16), o_ref.view(torch.int16))
     for t, r in zip((qg, kg, vg), (dq_ref, dk_ref, dv_ref)):
         assert torch.equal(t.grad.view(torch.int16), r.view(torch.int16))
+
+
+def test_malformed_cu_seqlens_stay_inside(fa):
+    """Offsets that break the rules (decreasing, past total, negative; a length above
+    max_seqlen) are clamped on the device: no write lands outside the operands. Each output
+    sits between NaN guard regions, which must come back untouched."""
+    import torch
+    H, d, T, G = 2, 64, 300, 4096
+    bits = FI.draw_bits((1, H, T, d), FI.BF16, 4700)
+    q, k, v, do = (_lib.to_device(bits[n][0].transpose(1, 0, 2), FI.BF16) for n in FI.TENSOR_ORDER)
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((G + n + G,), float("nan"), dtype=dtype, device=q.device)
+        return buf, buf[G:G + n].view(*shape)
+
+    cases = [
+        [0, 200, 100, 300],      # decreasing offsets
+        [0, 150, 5000],          # an offset past total
+        [-50, 120, 300],         # a negative offset
+        [0, 300],                # one sequence longer than max_seqlen (128)
+    ]
+    for cu_list in cases:
+        cu = torch.tensor(cu_list, dtype=torch.int32, device=q.device)
+        (ob, o), (lb, lse) = guarded((T, H, d), q.dtype), guarded((H, T), torch.float32)
+        (dqb, dq), (dkb, dk), (dvb, dv) = (guarded((T, H, d), q.dtype) for _ in range(3))
+        (db, delta) = guarded((H, T), torch.float32)
+        fa.fa_forward_ex(q, k, v, o, lse, True, d ** -0.5, cu_seqlens=cu, max_seqlen=128)
+        fa.fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, True, d ** -0.5, cu_seqlens=cu, max_seqlen=128)
+        torch.cuda.synchronize()
+        for name, buf in (("o", ob), ("lse", lb), ("dq", dqb), ("dk", dkb), ("dv", dvb), ("delta", db)):
+            assert torch.isnan(buf[:G]).all() and torch.isnan(buf[-G:]).all(), (cu_list, name)
