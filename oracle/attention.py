@@ -17,8 +17,13 @@ surrounding prose fixes them, and the readings are listed in the design notes):
 * scores  S = scale * Q K^T ("Triton 05: Flash Attention", section "코드 라인별 설명
   (Forward)", inner-loop step 1; "FlashAttention·FA4·FP4", section "첫 번째 비용":
   S = QK^T/sqrt(d)); the scale is applied before masking and the row max;
-* causal mask: key j is visible to query i iff j <= i ("Triton 05", section "Causal
-  Masking": future tokens are blocked by -inf);
+* causal mask: key j is visible to query i iff j <= i + (Nk - Nq) ("Triton 05", section
+  "Causal Masking": future tokens are blocked by -inf). With Nq = Nk this is j <= i. With
+  Nq != Nk the queries are read as the last Nq positions of the Nk-long sequence
+  (bottom-right alignment), the reading under which a decode query -- one new token
+  against the whole cache ("FlashAttentionを1から", section "その後の版と、推論での事情")
+  -- sees every key;
+* a row that sees no key (Nq > Nk, causal) has P = 0, O = 0 and LSE = -inf;
 * safe softmax along each row: P_ij = exp(S_ij - m_i) / sum_k exp(S_ik - m_i),
   m_i = max_k S_ik ("FlashAttentionを1から", section "タイリングを阻む、softmaxという壁");
 * output O = P V, and the saved row statistic LSE_i = m_i + ln sum_j exp(S_ij - m_i),
@@ -44,6 +49,11 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def causal_hidden(rows, nq: int, nk: int) -> np.ndarray:
+    """Boolean (len(rows), nk): key j hidden from query row i iff j > i + (nk - nq)."""
+    return np.arange(nk)[None, :] > np.asarray(rows)[:, None] + (nk - nq)
+
+
 def scores(q, k, scale: float, causal: bool) -> np.ndarray:
     """S = scale * Q K^T, with S_ij = -inf where the causal mask hides key j from query i."""
     q = _as_f64(q)
@@ -51,17 +61,25 @@ def scores(q, k, scale: float, causal: bool) -> np.ndarray:
     s = scale * (q @ k.T)
     if causal:
         nq, nk = s.shape
-        hidden = np.arange(nk)[None, :] > np.arange(nq)[:, None]
-        s[hidden] = -np.inf
+        s[causal_hidden(np.arange(nq), nq, nk)] = -np.inf
     return s
 
 
 def softmax_rows(s: np.ndarray):
-    """Safe softmax over each row. Returns (P, m, l) with m the row max, l = sum exp(s - m)."""
+    """Safe softmax over each row. Returns (P, m, l) with m the row max, l = sum exp(s - m).
+
+    A row with every entry -inf (it sees no key) gets P = 0, m = -inf, l = 0."""
     m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
+    empty = m == -np.inf
+    e = np.exp(s - np.where(empty, 0.0, m)[:, None])
     l = e.sum(axis=1)
-    return e / l[:, None], m, l
+    return e / np.where(empty, 1.0, l)[:, None], m, l
+
+
+def _lse(m, l):
+    """LSE = m + ln l, and -inf for a row that sees no key."""
+    empty = m == -np.inf
+    return np.where(empty, -np.inf, np.where(empty, 0.0, m) + np.log(np.where(empty, 1.0, l)))
 
 
 def forward(q, k, v, scale: float, causal: bool, return_p: bool = False):
@@ -69,7 +87,7 @@ def forward(q, k, v, scale: float, causal: bool, return_p: bool = False):
     s = scores(q, k, scale, causal)
     p, m, l = softmax_rows(s)
     o = p @ _as_f64(v)
-    lse = m + np.log(l)
+    lse = _lse(m, l)
     if return_p:
         return o, lse, p
     return o, lse
@@ -87,10 +105,9 @@ def forward_rows(q, k, v, scale: float, causal: bool, rows):
     k = _as_f64(k)
     s = scale * (q[rows] @ k.T)
     if causal:
-        hidden = np.arange(k.shape[0])[None, :] > rows[:, None]
-        s[hidden] = -np.inf
+        s[causal_hidden(rows, q.shape[0], k.shape[0])] = -np.inf
     p, m, l = softmax_rows(s)
-    return p @ _as_f64(v), m + np.log(l)
+    return p @ _as_f64(v), _lse(m, l)
 
 
 def backward(q, k, v, do, scale: float, causal: bool):

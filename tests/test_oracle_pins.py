@@ -248,11 +248,71 @@ def check_gradient_invariants(fwd, bwd):
     return errs
 
 
+def check_rectangular_causal(fwd, bwd):
+    """Nq != Nk with the causal mask: the queries are the last Nq positions.
+
+    * a rectangular problem is the last Nq rows of the square one (O, LSE, dQ), and its
+      dK, dV are the square problem's with dO zero on the rows it lacks (the loss is
+      linear in dO);
+    * one causal query sees every key: it equals the unmasked result;
+    * Nq > Nk: the first Nq - Nk rows see no key (O = 0, LSE = -inf, dQ = 0) and the
+      rest are the square problem on the last Nk queries;
+    * a tiny case written out with scalar loops.
+    """
+    errs = []
+    nk, d = 12, 5
+    qf, k, v, dof = _rand(121, nk, d), _rand(122, nk, d), _rand(123, nk, d), _rand(124, nk, d)
+    o_sq, lse_sq = fwd(qf, k, v, 0.6, True)
+    for nq in (1, 5):
+        o, lse = fwd(qf[-nq:], k, v, 0.6, True)
+        if not (np.allclose(o, o_sq[-nq:], atol=1e-13) and np.allclose(lse, lse_sq[-nq:], atol=1e-13)):
+            errs.append(f"rectangular causal (nq={nq}) != last rows of the square problem")
+        r = bwd(qf[-nq:], k, v, dof[-nq:], 0.6, True)
+        do_pad = dof.copy()
+        do_pad[:-nq] = 0.0
+        rs = bwd(qf, k, v, do_pad, 0.6, True)
+        if not (np.allclose(r["dq"], rs["dq"][-nq:], atol=1e-12) and np.allclose(r["dk"], rs["dk"], atol=1e-12)
+                and np.allclose(r["dv"], rs["dv"], atol=1e-12)):
+            errs.append(f"rectangular causal gradients (nq={nq}) != square problem with dO zero-padded")
+    o1, l1 = fwd(qf[:1], k, v, 0.6, True)
+    o2, l2 = fwd(qf[:1], k, v, 0.6, False)
+    if not (np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)):
+        errs.append("a single causal query does not see every key")
+    # Nq > Nk
+    q8 = _rand(125, 8, d)
+    o, lse = fwd(q8, k[:5], v[:5], 0.6, True)
+    o5, lse5 = fwd(q8[3:], k[:5], v[:5], 0.6, True)
+    if not (np.all(o[:3] == 0.0) and np.all(lse[:3] == -np.inf)):
+        errs.append("rows that see no key: O != 0 or LSE != -inf")
+    if not (np.allclose(o[3:], o5, atol=1e-14) and np.allclose(lse[3:], lse5, atol=1e-14)):
+        errs.append("Nq > Nk: visible rows != square problem on the last Nk queries")
+    r = bwd(q8, k[:5], v[:5], dof[:8], 0.6, True)
+    r5 = bwd(q8[3:], k[:5], v[:5], dof[3:8], 0.6, True)
+    if not (np.all(r["dq"][:3] == 0.0) and np.allclose(r["dk"], r5["dk"], atol=1e-12)
+            and np.allclose(r["dv"], r5["dv"], atol=1e-12)):
+        errs.append("Nq > Nk gradients")
+    # scalar loops: 3 queries, 7 keys, query i sees keys j <= i + 4
+    q3, k7, v7 = _rand(126, 3, 2), _rand(127, 7, 2), _rand(128, 7, 2)
+    o, lse = fwd(q3, k7, v7, 0.9, True)
+    for i in range(3):
+        sc = [0.9 * sum(q3[i, c] * k7[j, c] for c in range(2)) for j in range(i + 5)]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        tot = sum(w)
+        for c in range(2):
+            ref = sum(w[j] * v7[j, c] for j in range(len(w))) / tot
+            if not abs(o[i, c] - ref) < 1e-13:
+                errs.append(f"scalar-loop rectangular causal row {i}")
+        if not abs(lse[i] - (mx + math.log(tot))) < 1e-13:
+            errs.append(f"scalar-loop rectangular causal LSE row {i}")
+    return errs
+
+
 ALL_CHECKS = [
     check_worked_example_30, check_worked_example_fa2, check_causal_row0_and_last,
     check_single_key, check_equal_keys, check_permutations, check_block_invariance,
     check_library_logsumexp, check_torch_sdpa, check_finite_differences,
-    check_gradient_invariants,
+    check_gradient_invariants, check_rectangular_causal,
 ]
 
 
@@ -346,19 +406,19 @@ def _mutant_forward(kind):
             s = q @ k.T
         if causal:
             nq, nk = s.shape
-            jj, ii = np.arange(nk)[None, :], np.arange(nq)[:, None]
+            jj, ii = np.arange(nk)[None, :], np.arange(nq)[:, None] + (nk - nq)
             hidden = jj >= ii if kind == "mask_hides_diagonal" else (jj > ii + 1 if kind == "mask_shows_next" else jj > ii)
             if kind == "mask_transposed":
                 hidden = jj < ii
+            if kind == "mask_top_left":
+                hidden = jj > np.arange(nq)[:, None]
             s = np.where(hidden, -np.inf, s)
-        m = s.max(axis=1)
-        e = np.exp(s - m[:, None])
-        l = e.sum(axis=1)
-        p = e / l[:, None]
+        p, m, l = A.softmax_rows(s)
         o = p @ v
-        lse = m + (np.log2(l) if kind == "lse_base2" else np.log(l))
-        if kind == "lse_missing_max":
-            lse = np.log(l)
+        with np.errstate(divide="ignore"):
+            lse = m + (np.log2(l) if kind == "lse_base2" else np.log(l))
+            if kind == "lse_missing_max":
+                lse = np.log(l)
         return o, lse
     return fwd
 
@@ -395,7 +455,7 @@ def _mutant_backward(kind):
 
 
 FWD_MUTANTS = ["no_scale", "mask_hides_diagonal", "mask_shows_next", "mask_transposed",
-               "lse_base2", "lse_missing_max"]
+               "lse_base2", "lse_missing_max", "mask_top_left"]
 BWD_MUTANTS = ["dp_uses_k", "drop_jacobian_term", "jacobian_sign", "dk_not_transposed",
                "dq_missing_scale", "dv_not_transposed"]
 
