@@ -32,7 +32,7 @@ FA_ERR_HIP = 3
 
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_splitkv", "fa_forward_splitkv_workspace_bytes", "fa_backward",
                     "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_forward_ex", "fa_backward_ex",
-                    "fa_status_string")
+                    "fa_forward_splitkv_ex", "fa_forward_splitkv_ex_workspace_bytes", "fa_status_string")
 
 
 class FAStrides(ctypes.Structure):
@@ -41,10 +41,12 @@ class FAStrides(ctypes.Structure):
 
 
 class FAProblem(ctypes.Structure):
-    """fa_problem: shape, optional device cu_seqlens (variable lengths), mask, scale, dtype."""
+    """fa_problem: shape, optional device cu_seqlens (variable lengths), mask, scale, dtype, and
+    the key side's length bound / offsets / row count when they differ from the queries'."""
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
                 ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int), ("causal", ctypes.c_int),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("N_k", ctypes.c_int),
+                ("cu_seqlens_k", ctypes.c_void_p), ("total_k", ctypes.c_int)]
 
 _lib = None
 
@@ -83,6 +85,10 @@ def load_library() -> ctypes.CDLL:
     lib.fa_forward_ex.restype = i
     lib.fa_backward_ex.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, S, vp, vp, S, vp, S, vp, S, vp, vp]
     lib.fa_backward_ex.restype = i
+    lib.fa_forward_splitkv_ex.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, i, vp, ctypes.c_size_t, vp]
+    lib.fa_forward_splitkv_ex.restype = i
+    lib.fa_forward_splitkv_ex_workspace_bytes.argtypes = [P, i]
+    lib.fa_forward_splitkv_ex_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -310,41 +316,69 @@ def _ex_operand(name, t, shape, dtype, layout, varlen):
     return FAStrides(st[0], st[2], st[1])
 
 
-def _ex_problem(q, layout, cu_seqlens, max_seqlen, causal, scale):
-    """(problem, operand shape, statistics shape, varlen) of a strided / variable-length call."""
+def _check_offsets(name, cu):
     import torch
+    if not cu.is_cuda or cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor of B+1 offsets")
+
+
+def _ex_problem(q, k, layout, cu_seqlens, max_seqlen, causal, scale, cu_seqlens_k=None, max_seqlen_k=None):
+    """(problem, query-side shape, key-side shape, statistics shape, varlen) of a strided /
+    variable-length call. The key side (k, v, dk, dv) may have another row count than q."""
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {LAYOUTS}")
+    if k is None or k.dim() != q.dim():
+        raise ValueError("k must have as many dimensions as q")
     if cu_seqlens is not None:
         if q.dim() != 3:
             raise ValueError("with cu_seqlens, q is (total, H, d)")
-        if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
-            raise ValueError("cu_seqlens must be a contiguous int32 GPU tensor of B+1 offsets")
+        _check_offsets("cu_seqlens", cu_seqlens)
         if max_seqlen is None:
             raise ValueError("max_seqlen (the longest sequence) is required with cu_seqlens")
         T, H, d = q.shape
         B = cu_seqlens.numel() - 1
+        if cu_seqlens_k is not None:
+            _check_offsets("cu_seqlens_k", cu_seqlens_k)
+            if cu_seqlens_k.numel() != B + 1:
+                raise ValueError("cu_seqlens_k must hold as many offsets as cu_seqlens")
+            if max_seqlen_k is None:
+                raise ValueError("max_seqlen_k is required with cu_seqlens_k")
+            Tk, cuk, nk = k.shape[0], ctypes.c_void_p(cu_seqlens_k.data_ptr()), int(max_seqlen_k)
+        else:
+            if max_seqlen_k is not None:
+                raise ValueError("max_seqlen_k needs cu_seqlens_k")
+            Tk, cuk, nk = T, None, 0
         prob = FAProblem(B, H, int(max_seqlen), d, ctypes.c_void_p(cu_seqlens.data_ptr()), T, int(bool(causal)),
-                         float(scale), _dtype_code(q))
-        return prob, (T, H, d), (H, T), True
+                         float(scale), _dtype_code(q), nk, cuk, Tk if cu_seqlens_k is not None else 0)
+        return prob, (T, H, d), (Tk, H, d), (H, T), True
+    if cu_seqlens_k is not None or max_seqlen_k is not None:
+        raise ValueError("cu_seqlens_k / max_seqlen_k need cu_seqlens")
     if q.dim() != 4:
         raise ValueError("q is (B, H, N, d) or (B, N, H, d)")
     if layout == "bhnd":
         B, H, N, d = q.shape
+        Nk = k.shape[2]
+        kshape = (B, H, Nk, d)
     else:
         B, N, H, d = q.shape
-    prob = FAProblem(B, H, N, d, None, 0, int(bool(causal)), float(scale), _dtype_code(q))
-    return prob, tuple(q.shape), (B, H, N), False
+        Nk = k.shape[1]
+        kshape = (B, Nk, H, d)
+    prob = FAProblem(B, H, N, d, None, 0, int(bool(causal)), float(scale), _dtype_code(q), Nk, None, 0)
+    return prob, tuple(q.shape), kshape, (B, H, N), False
 
 
 def fa_forward_ex(q, k, v, o, lse, causal: bool, scale: float, layout: str = "bnhd", cu_seqlens=None,
-                  max_seqlen=None, stream=None) -> None:
+                  max_seqlen=None, stream=None, cu_seqlens_k=None, max_seqlen_k=None) -> None:
     """Forward on strided operands: (B,H,N,d) or (B,N,H,d) views whose head dim is contiguous,
     or, with cu_seqlens (int32, B+1 offsets on the GPU), packed (total, H, d) sequences; lse is
-    (B, H, N) or, with cu_seqlens, (H, total) float32, or None."""
+    (B, H, N) or, with cu_seqlens, (H, total) float32, or None. k and v may hold another
+    number of rows than q (N_k keys; packed: cu_seqlens_k / max_seqlen_k); the causal mask
+    then aligns the queries with the last keys."""
     import torch
-    prob, shape, sshape, varlen = _ex_problem(q, layout, cu_seqlens, max_seqlen, causal, scale)
-    ops = [_ex_operand(n, t, shape, q.dtype, layout, varlen) for n, t in (("q", q), ("k", k), ("v", v), ("o", o))]
+    prob, qshape, kshape, sshape, varlen = _ex_problem(q, k, layout, cu_seqlens, max_seqlen, causal, scale,
+                                                       cu_seqlens_k, max_seqlen_k)
+    ops = [_ex_operand(n, t, sh, q.dtype, layout, varlen)
+           for n, t, sh in (("q", q, qshape), ("k", k, kshape), ("v", v, kshape), ("o", o, qshape))]
     if lse is not None:
         _check_bhnd("lse", lse, sshape, torch.float32)
     st = load_library().fa_forward_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2], _ptr(o),
@@ -353,14 +387,49 @@ def fa_forward_ex(q, k, v, o, lse, causal: bool, scale: float, layout: str = "bn
         raise FAError(st, "fa_forward_ex")
 
 
-def fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, causal: bool, scale: float, layout: str = "bnhd",
-                   cu_seqlens=None, max_seqlen=None, stream=None) -> None:
-    """Backward on strided operands / packed sequences (same layouts as fa_forward_ex); delta
-    is a float32 workspace shaped like lse."""
+def fa_forward_splitkv_ex_workspace_bytes(q, k, num_splits: int, layout: str = "bnhd", cu_seqlens=None,
+                                          max_seqlen=None, cu_seqlens_k=None, max_seqlen_k=None) -> int:
+    """Workspace bytes fa_forward_splitkv_ex needs for these operands (0 for invalid ones)."""
+    prob = _ex_problem(q, k, layout, cu_seqlens, max_seqlen, False, 1.0, cu_seqlens_k, max_seqlen_k)[0]
+    return int(load_library().fa_forward_splitkv_ex_workspace_bytes(ctypes.byref(prob), int(num_splits)))
+
+
+def fa_forward_splitkv_ex(q, k, v, o, lse, causal: bool, scale: float, num_splits: int, workspace=None,
+                          layout: str = "bnhd", cu_seqlens=None, max_seqlen=None, stream=None, cu_seqlens_k=None,
+                          max_seqlen_k=None) -> None:
+    """fa_forward_ex with every Q tile's keys cut into num_splits ranges (decode: one query
+    against a long key cache); workspace is a float32 GPU tensor of at least
+    fa_forward_splitkv_ex_workspace_bytes bytes (allocated here when None)."""
     import torch
-    prob, shape, sshape, varlen = _ex_problem(q, layout, cu_seqlens, max_seqlen, causal, scale)
-    names = (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv))
-    ops = [_ex_operand(n, t, shape, q.dtype, layout, varlen) for n, t in names]
+    prob, qshape, kshape, sshape, varlen = _ex_problem(q, k, layout, cu_seqlens, max_seqlen, causal, scale,
+                                                       cu_seqlens_k, max_seqlen_k)
+    ops = [_ex_operand(n, t, sh, q.dtype, layout, varlen)
+           for n, t, sh in (("q", q, qshape), ("k", k, kshape), ("v", v, kshape), ("o", o, qshape))]
+    if lse is not None:
+        _check_bhnd("lse", lse, sshape, torch.float32)
+    lib = load_library()
+    need = int(lib.fa_forward_splitkv_ex_workspace_bytes(ctypes.byref(prob), int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
+    if not workspace.is_cuda or workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 GPU tensor")
+    st = lib.fa_forward_splitkv_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2], _ptr(o),
+                                   ops[3], _ptr(lse), int(num_splits), _ptr(workspace),
+                                   workspace.numel() * 4, _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_splitkv_ex")
+
+
+def fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, causal: bool, scale: float, layout: str = "bnhd",
+                   cu_seqlens=None, max_seqlen=None, stream=None, cu_seqlens_k=None, max_seqlen_k=None) -> None:
+    """Backward on strided operands / packed sequences (same layouts and key-side rules as
+    fa_forward_ex); delta is a float32 workspace shaped like lse."""
+    import torch
+    prob, qshape, kshape, sshape, varlen = _ex_problem(q, k, layout, cu_seqlens, max_seqlen, causal, scale,
+                                                       cu_seqlens_k, max_seqlen_k)
+    names = (("q", q, qshape), ("k", k, kshape), ("v", v, kshape), ("o", o, qshape), ("do", do, qshape),
+             ("dq", dq, qshape), ("dk", dk, kshape), ("dv", dv, kshape))
+    ops = [_ex_operand(n, t, sh, q.dtype, layout, varlen) for n, t, sh in names]
     for name, t in (("lse", lse), ("delta", delta)):
         _check_bhnd(name, t, sshape, torch.float32)
     st = load_library().fa_backward_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2],
@@ -385,7 +454,7 @@ def _autograd_function_ex():
 
     class FlashAttentionExFunction(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, causal, scale, cu_seqlens, max_seqlen):
+        def forward(ctx, q, k, v, causal, scale, cu_seqlens, max_seqlen, cu_seqlens_k, max_seqlen_k):
             q, k, v = _row_major(q), _row_major(k), _row_major(v)
             o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
             if cu_seqlens is None:
@@ -393,20 +462,21 @@ def _autograd_function_ex():
                 lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
             else:
                 lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-            fa_forward_ex(q, k, v, o, lse, causal, scale, "bnhd", cu_seqlens, max_seqlen)
-            ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
-            ctx.causal, ctx.scale, ctx.max_seqlen = causal, scale, max_seqlen
+            fa_forward_ex(q, k, v, o, lse, causal, scale, "bnhd", cu_seqlens, max_seqlen, None, cu_seqlens_k,
+                          max_seqlen_k)
+            ctx.save_for_backward(q, k, v, o, lse, cu_seqlens, cu_seqlens_k)
+            ctx.causal, ctx.scale, ctx.max_seqlen, ctx.max_seqlen_k = causal, scale, max_seqlen, max_seqlen_k
             return o
 
         @staticmethod
         def backward(ctx, do):
-            q, k, v, o, lse, cu_seqlens = ctx.saved_tensors
+            q, k, v, o, lse, cu_seqlens, cu_seqlens_k = ctx.saved_tensors
             do = _row_major(do)
             dq, dk, dv = (torch.empty(t.shape, dtype=t.dtype, device=t.device) for t in (q, k, v))
             delta = torch.empty_like(lse)
             fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, ctx.causal, ctx.scale, "bnhd", cu_seqlens,
-                           ctx.max_seqlen)
-            return dq, dk, dv, None, None, None, None
+                           ctx.max_seqlen, None, cu_seqlens_k, ctx.max_seqlen_k)
+            return dq, dk, dv, None, None, None, None, None, None
 
     _AUTOGRAD_EX = FlashAttentionExFunction
     return FlashAttentionExFunction
@@ -414,17 +484,21 @@ def _autograd_function_ex():
 
 def flash_attn_func(q, k, v, causal: bool = False, scale: float | None = None):
     """Differentiable exact attention on (B, N, H, d) GPU tensors (any strides with a
-    contiguous head dim, e.g. slices of a packed (B, N, 3, H, d) tensor)."""
+    contiguous head dim, e.g. slices of a packed (B, N, 3, H, d) tensor); k and v may hold
+    N_k != N rows (the causal mask then aligns the queries with the last keys)."""
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    return _autograd_function_ex().apply(q, k, v, causal, scale, None, None)
+    return _autograd_function_ex().apply(q, k, v, causal, scale, None, None, None, None)
 
 
-def flash_attn_varlen_func(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None):
+def flash_attn_varlen_func(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, scale: float | None = None,
+                           cu_seqlens_k=None, max_seqlen_k: int | None = None):
     """Differentiable exact attention over packed variable-length sequences: q, k, v are
     (total, H, d) GPU tensors, sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1] - 1
     (int32 GPU tensor of B+1 offsets), max_seqlen bounds every length. Each sequence attends
-    only to itself ("FlashAttentionを1から", section "現場ではこう使う")."""
+    only to itself ("FlashAttentionを1から", section "現場ではこう使う"). With cu_seqlens_k /
+    max_seqlen_k the key rows of sequence b are k[cu_seqlens_k[b] : cu_seqlens_k[b+1]]."""
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    return _autograd_function_ex().apply(q, k, v, causal, scale, cu_seqlens, int(max_seqlen))
+    mk = None if max_seqlen_k is None else int(max_seqlen_k)
+    return _autograd_function_ex().apply(q, k, v, causal, scale, cu_seqlens, int(max_seqlen), cu_seqlens_k, mk)

@@ -43,35 +43,46 @@ struct Operand {
   fa::Strides st{};
 };
 
-// Shape checks shared by every entry point. rows_per_head: N (fixed) or total (varlen).
+// Key-side length bound, offsets and row count of a problem (defaults: the query side's).
+int nk_of(const fa_problem& p) { return p.N_k > 0 ? p.N_k : p.N; }
+const int* cuk_of(const fa_problem& p) { return p.cu_seqlens_k ? p.cu_seqlens_k : p.cu_seqlens; }
+int totalk_of(const fa_problem& p) { return p.cu_seqlens_k ? p.total_k : p.total; }
+// Rows of a query-side / key-side operand.
+long long qrows(const fa_problem& p) { return p.cu_seqlens ? p.total : p.N; }
+long long krows(const fa_problem& p) { return p.cu_seqlens ? totalk_of(p) : nk_of(p); }
+
+// Shape checks shared by every entry point.
 int check_shape(const fa_problem& p) {
-  if (p.B <= 0 || p.H <= 0 || p.d <= 0 || p.N <= 0) return FA_ERR_INVALID_ARG;
+  if (p.B <= 0 || p.H <= 0 || p.d <= 0 || p.N <= 0 || p.N_k < 0) return FA_ERR_INVALID_ARG;
   if (p.dtype != FA_FP16 && p.dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (p.causal != 0 && p.causal != 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(p.scale) || !(p.scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (p.cu_seqlens != nullptr && (p.total < 0 || !aligned16(p.cu_seqlens))) return FA_ERR_INVALID_ARG;
+  if (p.cu_seqlens_k != nullptr && (p.cu_seqlens == nullptr || p.total_k < 0 || !aligned16(p.cu_seqlens_k)))
+    return FA_ERR_INVALID_ARG;
   const long long bh = (long long)p.B * p.H;
   if (bh > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   // head dims: multiples of 8 up to 256, run on the 64-, 128- or 256-wide kernels with the
   // columns past d zero on chip
   if (p.d % 8 != 0 || p.d > 256) return FA_ERR_UNSUPPORTED;
-  if (p.N > (1 << 30)) return FA_ERR_UNSUPPORTED;
-  // Grids: (N / 64) * B*H tile workgroups, and (statistics rows / 4) * heads row blocks, in
-  // one 32-bit grid dimension.
+  if (p.N > (1 << 30) || nk_of(p) > (1 << 30)) return FA_ERR_UNSUPPORTED;
+  // Grids: (N / 64) * B*H and (N_k / 64) * B*H tile workgroups, and (statistics rows / 4) *
+  // heads row blocks, in one 32-bit grid dimension.
   if (((long long)p.N + 63) / 64 * bh > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (((long long)nk_of(p) + 63) / 64 * bh > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   const long long stat = p.cu_seqlens ? (long long)p.H * p.total : bh * p.N;
   if (stat / 4 + bh > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
-// A 16-bit operand of the problem with strides s; FA_OK or FA_ERR_INVALID_ARG.
-int make_operand(const fa_problem& p, const void* data, const fa_strides& s, Operand* op) {
+// A 16-bit operand of the problem with strides s and `rows` rows per head (qrows or krows);
+// FA_OK or FA_ERR_INVALID_ARG.
+int make_operand(const fa_problem& p, const void* data, const fa_strides& s, long long rows, Operand* op) {
   if (!data || !aligned16(data)) return FA_ERR_INVALID_ARG;
   const bool varlen = p.cu_seqlens != nullptr;
   const long long sb = varlen ? 0 : s.batch;
   if (sb < 0 || s.head < 0 || s.row < p.d || s.row > kMaxRowStride) return FA_ERR_INVALID_ARG;
   if ((sb | s.head | s.row) & 7) return FA_ERR_INVALID_ARG;
-  const long long rows = varlen ? p.total : p.N;
   op->base = reinterpret_cast<uintptr_t>(data);
   op->ndims = 0;
   op->dims[op->ndims++] = Dim{1, p.d};
@@ -180,6 +191,9 @@ fa::Geom geom_of(const fa_problem& p) {
   g.cu = p.cu_seqlens;
   g.T = p.cu_seqlens ? p.total : 0;
   g.dh = p.d;
+  g.Nk = nk_of(p);
+  g.cuk = p.cu_seqlens ? cuk_of(p) : nullptr;
+  g.Tk = p.cu_seqlens ? totalk_of(p) : 0;
   return g;
 }
 
@@ -202,6 +216,9 @@ fa_problem fixed_problem(int B, int H, int N, int d, int causal, float scale, in
   p.causal = causal;
   p.scale = scale;
   p.dtype = dtype;
+  p.N_k = 0;
+  p.cu_seqlens_k = nullptr;
+  p.total_k = 0;
   return p;
 }
 
@@ -217,6 +234,11 @@ long long splitkv_bytes(long long rows, int d, int splits) {
   return (long long)splits * rows * (kernel_d(d) + 2) * 4;
 }
 
+// Packed batches with no rows: the forward has no query; the backward also needs no key (a
+// key no query sees still gets dK = dV = 0 written).
+bool nothing_to_do_fwd(const fa_problem& p) { return p.cu_seqlens != nullptr && p.total == 0; }
+bool nothing_to_do_bwd(const fa_problem& p) { return p.cu_seqlens != nullptr && p.total == 0 && totalk_of(p) == 0; }
+
 int forward_impl(const fa_problem* pp, const void* q, const fa_strides& sq, const void* k, const fa_strides& sk,
                  const void* v, const fa_strides& sv, void* o, const fa_strides& so, float* lse, int splits,
                  float* part, size_t part_bytes, void* stream) {
@@ -225,10 +247,10 @@ int forward_impl(const fa_problem* pp, const void* q, const fa_strides& sq, cons
   int st = check_shape(p);
   if (st != FA_OK) return st;
   Operand ins[3], outs[3];
-  if ((st = make_operand(p, q, sq, &ins[0])) != FA_OK) return st;
-  if ((st = make_operand(p, k, sk, &ins[1])) != FA_OK) return st;
-  if ((st = make_operand(p, v, sv, &ins[2])) != FA_OK) return st;
-  if ((st = make_operand(p, o, so, &outs[0])) != FA_OK) return st;
+  if ((st = make_operand(p, q, sq, qrows(p), &ins[0])) != FA_OK) return st;
+  if ((st = make_operand(p, k, sk, krows(p), &ins[1])) != FA_OK) return st;
+  if ((st = make_operand(p, v, sv, krows(p), &ins[2])) != FA_OK) return st;
+  if ((st = make_operand(p, o, so, qrows(p), &outs[0])) != FA_OK) return st;
   int nout = 1;
   const long long rows = stat_count(p);
   if (lse) {
@@ -244,7 +266,7 @@ int forward_impl(const fa_problem* pp, const void* q, const fa_strides& sq, cons
     if (((long long)p.N + 127) / 128 * splits * ((long long)p.B * p.H) > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   }
   if ((st = check_overlaps(ins, 3, outs, nout)) != FA_OK) return st;
-  if (p.cu_seqlens && p.total == 0) return FA_OK;
+  if (nothing_to_do_fwd(p)) return FA_OK;
   fa::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -291,14 +313,14 @@ int check_bwd(const fa_problem* pp, const void* q, const fa_strides& sq, const v
     const void* data;
     const fa_strides* s;
     fa::Strides* dst;
-    bool out;
-  } t16[] = {{q, &sq, &a->sq, false},   {k, &sk, &a->sk, false},   {v, &sv, &a->sv, false},
-             {o, &so, &a->so, false},   {dO, &sdo, &a->sdo, false}, {dq, &sdq, &a->sdq, true},
-             {dk, &sdk, &a->sdk, true}, {dv, &sdv, &a->sdv, true}};
+    bool out, key_side;
+  } t16[] = {{q, &sq, &a->sq, false, false},   {k, &sk, &a->sk, false, true},   {v, &sv, &a->sv, false, true},
+             {o, &so, &a->so, false, false},   {dO, &sdo, &a->sdo, false, false}, {dq, &sdq, &a->sdq, true, false},
+             {dk, &sdk, &a->sdk, true, true}, {dv, &sdv, &a->sdv, true, true}};
   for (const T16& t : t16) {
     *t.dst = fa::Strides{0, 0, 0};
     if (!t.data) continue;
-    if ((st = make_operand(p, t.data, *t.s, &op)) != FA_OK) return st;
+    if ((st = make_operand(p, t.data, *t.s, t.key_side ? krows(p) : qrows(p), &op)) != FA_OK) return st;
     *t.dst = op.st;
     if (t.out)
       outs[nout++] = op;
@@ -330,7 +352,6 @@ int check_bwd(const fa_problem* pp, const void* q, const fa_strides& sq, const v
   return FA_OK;
 }
 
-bool nothing_to_do(const fa_problem& p) { return p.cu_seqlens != nullptr && p.total == 0; }
 
 }  // namespace
 
@@ -363,6 +384,19 @@ int fa_forward_ex(const fa_problem* p, const void* q, fa_strides sq, const void*
   return forward_impl(p, q, sq, k, sk, v, sv, o, so, lse, 0, nullptr, 0, stream);
 }
 
+int fa_forward_splitkv_ex(const fa_problem* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                          const void* v, fa_strides sv, void* o, fa_strides so, float* lse, int num_splits,
+                          float* workspace, size_t workspace_bytes, void* stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  return forward_impl(p, q, sq, k, sk, v, sv, o, so, lse, num_splits, workspace, workspace_bytes, stream);
+}
+
+size_t fa_forward_splitkv_ex_workspace_bytes(const fa_problem* p, int num_splits) {
+  if (!p || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  if (check_shape(*p) != FA_OK) return 0;
+  return (size_t)splitkv_bytes(stat_count(*p), p->d, num_splits);
+}
+
 size_t fa_forward_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
   if (num_splits < 1 || num_splits > kMaxSplits) return 0;
   const fa_problem p = fixed_problem(B, H, N, d, 0, 1.0f, FA_BF16);
@@ -388,7 +422,7 @@ int fa_backward_ex(const fa_problem* p, const void* q, fa_strides sq, const void
   int st = check_bwd(p, q, sq, k, sk, v, sv, o, so, dO, sdo, lse, dq, sdq, dk, sdk, dv, sdv, delta, true, true,
                      true, true, &a);
   if (st != FA_OK) return st;
-  if (nothing_to_do(*p)) return FA_OK;
+  if (nothing_to_do_bwd(*p)) return FA_OK;
   a.stream = stream;
   if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_HIP;
   if (fa::launch_bwd_dkv(a) != hipSuccess) return FA_ERR_HIP;

@@ -100,13 +100,15 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
   const Seq sq_ = seq_of(geo, bh);
-  const int N = sq_.n;
+  const int N = sq_.n;    // query rows of this sequence
+  const int NK = sq_.nk;  // key rows
+  const int off = NK - N;  // causal: query i sees key j iff j <= i + off
   const int n_qtiles = (N + BM - 1) / BM;
   if (pr >= (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles)) return;
   const int npass = (CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
   const uint16_t* Qh = seq_base(Q, sq, sq_);
-  const uint16_t* Kh = seq_base(K, sk, sq_);
-  const uint16_t* Vh = seq_base(V, sv, sq_);
+  const uint16_t* Kh = seq_base_k(K, sk, sq_);
+  const uint16_t* Vh = seq_base_k(V, sv, sq_);
   const uint16_t* dOh = seq_base(dO, sdo, sq_);
   uint16_t* dQh = seq_base(dQ, sdq, sq_);
   const int rsq = (int)sq.r, rsk = (int)sk.r, rsv = (int)sv.r, rsdo = (int)sdo.r, rsdq = (int)sdq.r;
@@ -117,16 +119,17 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
   const int q0 = qt * BM;
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  // Keys [0, kv_end) are visible to some row of the workgroup (none: dQ = 0).
+  const int kv_end = CAUSAL ? min(NK, max(0, q0 + BM + off)) : NK;
   const int ntiles = (kv_end + BN - 1) / BN;
   // Tiles [0, n_plain) have every key visible to every row of the workgroup: no mask.
-  const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
-  // Keys past N, and with the causal mask keys after the row, are hidden: key <= key_lim.
-  const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+  const int n_plain = CAUSAL ? min(NK, max(0, q0 + off + 1)) / BN : NK / BN;
+  // Keys past NK, and with the causal mask keys after row + off, are hidden: key <= key_lim.
+  const int key_lim = CAUSAL ? min(qrow + off, NK - 1) : NK - 1;
 
   const int dh = geo.dh;
-  stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, N, rsk, dh, wave);
-  stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, N, rsv, dh, wave);
+  stage_rows_swz_buf<D, BN, NW>(lds_k0, Kh, 0, NK, rsk, dh, wave);
+  stage_rows_swz_buf<D, BN, NW>(lds_v0, Vh, 0, NK, rsv, dh, wave);
 
   Frag qf[KS], dof[KS];
   float lse2, dl;
@@ -180,8 +183,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
     // this lane's row iff key <= key_lim, i.e. iff its compile-time offset is <= thr.
     const int thr = key_lim - t * BN - 4 * h;
     const int tn = min(t + 1, ntiles - 1);
-    const TileSrc rk = tile_src<D, BN>(Kh, tn * BN, N, rsk, dh);
-    const TileSrc rv = tile_src<D, BN>(Vh, tn * BN, N, rsv, dh);
+    const TileSrc rk = tile_src<D, BN>(Kh, tn * BN, NK, rsk, dh);
+    const TileSrc rv = tile_src<D, BN>(Vh, tn * BN, NK, rsv, dh);
     // fragment i of a K or V tile: key block i % KB (so consecutive MFMAs are independent),
     // k-step i / KB
     auto rfrag = [&](const uint16_t* tile, int i) {

@@ -71,16 +71,18 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
   const Seq sq_ = seq_of(geo, bh);
-  const int N = sq_.n;
-  const int n_ktiles = (N + BK - 1) / BK;
+  const int N = sq_.n;    // query rows of this sequence
+  const int NK = sq_.nk;  // key rows
+  const int off = NK - N;  // causal: query i sees key j iff j <= i + off
+  const int n_ktiles = (NK + BK - 1) / BK;
   if (pr >= (CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles)) return;
   const int npass = (CAUSAL && n_ktiles - 1 - pr != pr) ? 2 : 1;
   const uint16_t* Qh = seq_base(Q, sq, sq_);
-  const uint16_t* Kh = seq_base(K, sk, sq_);
-  const uint16_t* Vh = seq_base(V, sv, sq_);
+  const uint16_t* Kh = seq_base_k(K, sk, sq_);
+  const uint16_t* Vh = seq_base_k(V, sv, sq_);
   const uint16_t* dOh = seq_base(dO, sdo, sq_);
-  uint16_t* dKh = seq_base(dK, sdk, sq_);
-  uint16_t* dVh = seq_base(dV, sdv, sq_);
+  uint16_t* dKh = seq_base_k(dK, sdk, sq_);
+  uint16_t* dVh = seq_base_k(dV, sdv, sq_);
   const int rsq = (int)sq.r, rsk = (int)sk.r, rsv = (int)sv.r, rsdo = (int)sdo.r;
   const float* lse_h = LSE + sq_.stat;
   const float* dl_h = Delta + sq_.stat;
@@ -93,13 +95,31 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   const int key = kw0 + l32;
 
 
-  const int it_begin = CAUSAL ? (k0 / BQ) : 0;
+  // Query steps [it_begin, it_end) hold every query that sees a key of this tile (query i
+  // sees key j iff j <= i + off).
+  const int it_begin = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int it_end = (N + BQ - 1) / BQ;
 
   const int dh = geo.dh;
+  if (it_begin >= it_end) {
+    // No query sees these keys (more keys than queries, causal): dK = dV = 0.
+    if (key < NK) {
+      uint16_t* dk_row = dKh + (size_t)key * sdk.r;
+      uint16_t* dv_row = dVh + (size_t)key * sdv.r;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (db * 32 + 8 * g < dh) {
+            *reinterpret_cast<u32x2*>(dk_row + db * 32 + 8 * g + 4 * h) = u32x2{0u, 0u};
+            *reinterpret_cast<u32x2*>(dv_row + db * 32 + 8 * g + 4 * h) = u32x2{0u, 0u};
+          }
+    }
+    continue;
+  }
   // At two waves per SIMD registers are short: one lane offset serves all of a wave's copies.
   constexpr bool SHARE = D <= 128;
-  stage_rows_swz_buf<D, BK, NW, SHARE>(lds_v, Vh, k0, N, rsv, dh, wave);
+  stage_rows_swz_buf<D, BK, NW, SHARE>(lds_v, Vh, k0, NK, rsv, dh, wave);
   stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_q0, Qh, it_begin * BQ, N, rsq, dh, wave);
   stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_do0, dOh, it_begin * BQ, N, rsdo, dh, wave);
   if (wave == NW - 1) stage_stats_buf((FA_LDS float*)lds_st0, lse_h, dl_h, it_begin * BQ, N);
@@ -107,7 +127,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   // Pinned K fragments (B operand of S = Q K^T): lane holds K[key][16ks + 8h .. +7].
   Frag kf[KS];
   {
-    const bool ok = key < N;
+    const bool ok = key < NK;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks].v = gload16(Kh + (size_t)key * rsk + ks * 16 + h * 8, ok && ks * 16 + h * 8 < dh);
   }
@@ -150,10 +170,10 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     constexpr bool MASK = decltype(mask_tag)::value;
     const int qbase = it * BQ;
     // Register i holds query row qbase + 4h + 8(i/4) + (i%4) of this lane's key. It is visible
-    // iff the row is < N, the key is < N and (causal) the row is >= the key, i.e. iff the
+    // iff the row is < N, the key is < NK and (causal) row + off >= key, i.e. iff the
     // compile-time offset 8(i/4) + (i%4) lies in [vis_lo, vis_hi); one unsigned compare.
-    const int vis_lo = CAUSAL ? key - qbase - 4 * h : -(1 << 24);
-    const int vis_hi = key < N ? N - qbase - 4 * h : vis_lo;
+    const int vis_lo = CAUSAL ? key - off - qbase - 4 * h : -(1 << 24);
+    const int vis_hi = key < NK ? N - qbase - 4 * h : vis_lo;
     const uint32_t vis_span = (uint32_t)max(vis_hi - vis_lo, 0);
     // this wave's V rows: base offset re-materialised each step (kept opaque so the compiler
     // adds it per read instead of holding KS more loop-invariant addresses)
@@ -281,8 +301,10 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     step(mask_tag, it, lds_q0, lds_do0, lds_st0, lds_q1, lds_do1, (FA_LDS float*)lds_st1);
     step(mask_tag, it + 1, lds_q1, lds_do1, lds_st1, lds_q0, lds_do0, (FA_LDS float*)lds_st0);
   };
-  const bool key_tail = k0 + BK > N;
-  const int plain_begin = key_tail ? it_end : (CAUSAL ? min(it_begin + BK / BQ, it_end) : it_begin);
+  const bool key_tail = k0 + BK > NK;
+  // the first step whose rows all see every key of the tile: qbase + off >= k0 + BK - 1
+  const int full_from = max(0, k0 + BK - 1 - off);
+  const int plain_begin = key_tail ? it_end : (CAUSAL ? min(it_end, max(it_begin, (full_from + BQ - 1) / BQ)) : it_begin);
   const int plain_end = key_tail ? it_end : max(plain_begin, N / BQ);
   int it = it_begin;
   for (; it < plain_begin; it += 2) pair(Tr(), it);
@@ -291,7 +313,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   // No copy may still be landing in LDS when the workgroup retires.
   wait_async();
 
-  if (key < N) {
+  if (key < NK) {
     uint16_t* dk_row = dKh + (size_t)key * sdk.r;
     uint16_t* dv_row = dVh + (size_t)key * sdv.r;
 #pragma unroll
@@ -318,7 +340,7 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dkv_t(const BwdArgs& a) {
   constexpr int NW = 4;
   constexpr int BK = NW * 32;
-  const int n_ktiles = (a.g.N + BK - 1) / BK;
+  const int n_ktiles = (a.g.Nk + BK - 1) / BK;
   const long long grid = (long long)(CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles) * a.g.B * a.g.H;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,

@@ -402,12 +402,13 @@ constexpr int kSchedTrans = 0x400;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// The sequence a workgroup works on: head bh = b*H + h of the grid, its length n, the packed
-// row its row 0 is (0 for fixed lengths) and the index of its row 0 in LSE / delta. Values
-// read from cu are clamped (0 <= row0 <= row0 + n <= T, n <= N) and made wave-uniform.
+// The sequence a workgroup works on: head bh = b*H + h of the grid, its query and key
+// lengths n and nk, the packed rows its query and key row 0 are (0 for fixed lengths) and the
+// index of its query row 0 in LSE / delta. Values read from cu / cuk are clamped
+// (0 <= row0 <= row0 + n <= T, n <= N; likewise for the keys) and made wave-uniform.
 struct Seq {
-  int b, h, n;
-  long long row0, stat;
+  int b, h, n, nk;
+  long long row0, row0k, stat;
 };
 __device__ __forceinline__ Seq seq_of(const Geom& g, int bh) {
   Seq s;
@@ -419,18 +420,29 @@ __device__ __forceinline__ Seq seq_of(const Geom& g, int bh) {
     s.n = min(c1 - c0, g.N);
     s.row0 = c0;
     s.stat = (long long)s.h * g.T + c0;
+    const int k0 = min(max(__builtin_amdgcn_readfirstlane(g.cuk[s.b]), 0), g.Tk);
+    const int k1 = min(max(__builtin_amdgcn_readfirstlane(g.cuk[s.b + 1]), k0), g.Tk);
+    s.nk = min(k1 - k0, g.Nk);
+    s.row0k = k0;
   } else {
     s.n = g.N;
+    s.nk = g.Nk;
     s.row0 = 0;
+    s.row0k = 0;
     s.stat = (long long)bh * g.N;
   }
   return s;
 }
-// Row 0 of operand `base` (strides st) for sequence s (with variable lengths the caller
-// passes a zero batch stride: the packed row row0 already selects the sequence).
+// Row 0 of query-side operand `base` (strides st) for sequence s (with variable lengths the
+// caller passes a zero batch stride: the packed row row0 already selects the sequence).
 template <typename P>
 __device__ __forceinline__ P* seq_base(P* base, const Strides& st, const Seq& s) {
   return base + ((long long)s.b * st.b + (long long)s.h * st.h + s.row0 * st.r);
+}
+// Row 0 of key-side operand `base` (K, V, dK, dV) for sequence s.
+template <typename P>
+__device__ __forceinline__ P* seq_base_k(P* base, const Strides& st, const Seq& s) {
+  return base + ((long long)s.b * st.b + (long long)s.h * st.h + s.row0k * st.r);
 }
 
 // Statistics rows (LSE, delta, split-KV partial states) form (HH, Rh): HH = B*H heads of N

@@ -82,14 +82,16 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
   const Seq sq_ = seq_of(geo, bh);
-  const int N = sq_.n;
+  const int N = sq_.n;    // query rows of this sequence
+  const int NK = sq_.nk;  // key rows
+  const int off = NK - N;  // causal: query i sees key j iff j <= i + off
   const int n_qtiles = (N + BM - 1) / BM;
   const int sp = SPLIT ? pr % splits : 0;  // key range of this workgroup
   if (SPLIT ? pr / splits >= n_qtiles : pr >= (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles)) return;
   const int npass = (!SPLIT && CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
   const uint16_t* Qh = seq_base(Q, sq, sq_);
-  const uint16_t* Kh = seq_base(K, sk, sq_);
-  const uint16_t* Vh = seq_base(V, sv, sq_);
+  const uint16_t* Kh = seq_base_k(K, sk, sq_);
+  const uint16_t* Vh = seq_base_k(V, sv, sq_);
   uint16_t* Oh = seq_base(O, so, sq_);
   const int rsq = (int)sq.r, rsk = (int)sk.r, rsv = (int)sv.r, rso = (int)so.r;
   for (int pass = 0; pass < npass; ++pass) {
@@ -99,10 +101,25 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   const int q0 = qt * BM;
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  // Keys [0, kv_end) are visible to some row of the workgroup.
+  const int kv_end = CAUSAL ? min(NK, max(0, q0 + BM + off)) : NK;
   const int ntiles = (kv_end + BN - 1) / BN;
   // Tiles [0, n_plain) have every key visible to every row of the workgroup: no mask.
-  const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
+  const int n_plain = CAUSAL ? min(NK, max(0, q0 + off + 1)) / BN : NK / BN;
+  const int dh = geo.dh;
+  if (!SPLIT && ntiles == 0) {
+    // No row of this tile sees a key (more queries than keys, causal): O = 0, LSE = -inf.
+    if (qrow < N) {
+      uint16_t* orow = Oh + (size_t)qrow * rso;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (db * 32 + 8 * g < dh) *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = u32x2{0u, 0u};
+      if (LSE != nullptr && h == 0) LSE[sq_.stat + qrow] = -INFINITY;
+    }
+    continue;
+  }
   // This workgroup's key tiles [t0, last]: all of them, or its split's share.
   const int t0 = SPLIT ? (int)((long long)sp * ntiles / splits) : 0;
   const int t1 = SPLIT ? (int)((long long)(sp + 1) * ntiles / splits) : ntiles;
@@ -124,9 +141,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   }
   const int last = t1 - 1;
 
-  const int dh = geo.dh;
-  auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, N, rsk, dh, wave); };
-  auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, N, rsv, dh, wave); };
+  auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, NK, rsk, dh, wave); };
+  auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, NK, rsv, dh, wave); };
   stage_k(t0, lds_k0);
   stage_v(t0, lds_v0);
   stage_k(min(t0 + 1, last), lds_k1);
@@ -184,12 +200,12 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
       for (int ks = 1; ks < KS; ++ks) s[kb] = T::mfma(kfrag(ktile, kb * KS + ks), qf[ks], s[kb]);
     }
   };
-  // Masking. A key is visible to this lane's row iff key <= key_lim (keys past N, and with the
-  // causal mask keys after the row, are hidden). Register i of key block kb holds key
+  // Masking. A key is visible to this lane's row iff key <= key_lim (keys past NK, and with
+  // the causal mask keys after row + off, are hidden; key_lim < 0: the row sees no key). Register i of key block kb holds key
   // kbase + 4h + kb*32 + 8(i/4) + (i%4), so with thr = key_lim - kbase - 4h an element is
   // hidden iff the compile-time offset kb*32 + 8(i/4) + (i%4) exceeds thr: one compare and one
   // select per element.
-  const int key_lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+  const int key_lim = CAUSAL ? min(qrow + off, NK - 1) : NK - 1;
   auto mask_thr = [&](int t) { return key_lim - t * BN - 4 * h; };
   auto masked = [](float x, int kb, int i, int thr) {
     return (kb * 32 + 8 * (i >> 2) + (i & 3)) > thr ? -INFINITY : x;
@@ -284,8 +300,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     // Copies of K(t+2) and V(t+1): descriptors now, the copies themselves spread over the
     // chunks of [A] (issued all at once, the workgroup's waves queue behind each other in the
     // texture unit right after the barrier).
-    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 2, last) * BN, N, rsk, dh);
-    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, N, rsv, dh);
+    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 2, last) * BN, NK, rsk, dh);
+    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, NK, rsv, dh);
     constexpr int CPW = BN * D * 2 / 1024 / NW;  // copies per wave per tile
 
     // [A] S(t+1) on the matrix cores while the VALU exponentiates S(t). Written out as 16
@@ -434,7 +450,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     }
     continue;
   }
-  const float inv = 1.0f / l_tot;
+  // a row that saw no key (l = 0) gets O = 0 and LSE = -inf
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* orow = Oh + (size_t)qrow * rso;
 #pragma unroll
@@ -447,7 +464,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
         // columns db*32 + 8g + 4h .. +3 exist iff db*32 + 8g < dh (dh is a multiple of 8)
         if (db * 32 + 8 * g < dh) *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
       }
-    if (LSE != nullptr && h == 0) LSE[sq_.stat + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+    if (LSE != nullptr && h == 0) LSE[sq_.stat + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
   }  // pass
 }
@@ -488,12 +505,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     a2 = __builtin_fmaf(w, o[2], a2);
     a3 = __builtin_fmaf(w, o[3], a3);
   }
-  const float inv = 1.0f / L;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;  // a row that saw no key: O = 0, LSE = -inf
   u32x2 w2;
   w2[0] = T::pack2(a0 * inv, a1 * inv);
   w2[1] = T::pack2(a2 * inv, a3 * inv);
   if (sub * 4 < geo.dh) *reinterpret_cast<u32x2*>(O + stat_row_offset(geo, so, hh, r) + sub * 4) = w2;
-  if (sub == 0 && LSE != nullptr) LSE[row] = (Mr + __log2f(L)) * kLn2;
+  if (sub == 0 && LSE != nullptr) LSE[row] = L > 0.f ? (Mr + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D>

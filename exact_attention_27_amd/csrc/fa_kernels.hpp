@@ -14,17 +14,24 @@ struct Strides {
   long long b, h, r;
 };
 
-// Problem geometry. Fixed length (cu == nullptr): every sequence has N rows and LSE / delta
-// are (B, H, N) contiguous. Variable length: sequence b is rows [cu[b], cu[b+1]) of every
-// operand, N bounds every length, T is the number of rows in all, and LSE / delta are (H, T)
-// contiguous. A workgroup clamps what it reads from cu to [0, T] and lengths to N, so no
-// contents of cu lead it outside the operands.
+// Problem geometry. Query-side operands (Q, O, dO, dQ; LSE, delta) and key-side operands
+// (K, V, dK, dV) may have different lengths. Fixed length (cu == nullptr): every sequence
+// has N query rows and Nk key rows, and LSE / delta are (B, H, N) contiguous. Variable
+// length: sequence b is query rows [cu[b], cu[b+1]) and key rows [cuk[b], cuk[b+1]) of the
+// packed operands (T and Tk rows in all), N and Nk bound the lengths, and LSE / delta are
+// (H, T) contiguous. A workgroup clamps what it reads from cu / cuk to [0, T] / [0, Tk] and
+// the lengths to N / Nk, so no contents of them lead it outside the operands. With the causal
+// mask the queries are the last positions of their sequence: query i sees key j iff
+// j <= i + (nk - n).
 struct Geom {
   int B, H, N;
   const int* cu;
   int T;
   int dh;  // head dim of the operands: a multiple of 8, at most the kernel's D; the columns
            // [dh, D) of every tile are zero on chip and never stored
+  int Nk;
+  const int* cuk;
+  int Tk;
 };
 
 struct FwdArgs {

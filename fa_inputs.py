@@ -148,6 +148,14 @@ def draw_bits(shape, dtype: str, seed: int, q_mult: float = 1.0) -> dict:
     return out
 
 
+def draw_bits_rect(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int) -> dict:
+    """Inputs with Nq query rows and Nk key rows: draw_bits over max(Nq, Nk) rows, then Q and
+    dO keep their first Nq rows and K and V their first Nk (contiguous copies)."""
+    bits = draw_bits((B, H, max(Nq, Nk), d), dtype, seed)
+    rows = {"q": Nq, "k": Nk, "v": Nk, "do": Nq}
+    return {n: np.ascontiguousarray(bits[n][:, :, :rows[n]]) for n in TENSOR_ORDER}
+
+
 def draw_workload(w: Workload) -> dict:
     return draw_bits(w.shape, w.dtype, w.seed, w.q_mult)
 

@@ -163,6 +163,14 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, 
  *
  * fa_problem: the shape of one call.
  *   B, H, d, causal, scale, dtype  as for fa_forward().
+ *   N_k   key rows per sequence when they differ from the query rows (0: N_k = N). The
+ *         query-side operands (q, o, dO, dq; lse, delta) have N rows, the key-side ones
+ *         (k, v, dk, dv) N_k. With the causal mask the queries are the last N of the
+ *         N_k positions: query i sees key j iff j <= i + (N_k - N) (bottom-right; with
+ *         N = N_k this is j <= i). A query that sees no key (N > N_k) gets O = 0,
+ *         LSE = -inf and dQ = 0; a key no query sees gets dK = dV = 0. Decode is N = 1:
+ *         one new token against the whole cache ("FlashAttentionを1から", section
+ *         "その後の版と、推論での事情"), best served by fa_forward_splitkv_ex.
  *   cu_seqlens == NULL  every sequence has N rows; lse and delta are (B, H, N) float32.
  *   cu_seqlens != NULL  variable lengths ("FlashAttentionを1から", section "現場ではこう使う":
  *       padding every sequence to the longest pays for the padding; cumulative sequence
@@ -170,12 +178,13 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, 
  *       0 = cu[0] <= cu[1] <= ... <= cu[B] = total: sequence b is the packed rows
  *       [cu[b], cu[b+1]) of every operand (each operand holds `total` rows of H heads; the
  *       batch stride is ignored). N is an upper bound of every length (the grid is sized
- *       by it); lse and delta are (H, total) float32. Each sequence attends only to itself,
- *       with the causal mask top-left aligned within it. The library never reads
- *       cu_seqlens on the host: offsets outside [0, total] are clamped and lengths above
- *       N cut to N on the device, so no contents make a kernel read or write outside the
- *       operands, but a batch that breaks the rules above gets unspecified values.
- *       total may be 0 (nothing is enqueued).
+ *       by it); lse and delta are (H, total) float32. Each sequence attends only to itself.
+ *       Key-side rows follow cu_seqlens_k (B+1 offsets, total_k rows in all, lengths at
+ *       most N_k) when it is not NULL, else cu_seqlens. The library never reads these
+ *       arrays on the host: offsets outside [0, total] ([0, total_k]) are clamped and
+ *       lengths above N (N_k) cut on the device, so no contents make a kernel read or
+ *       write outside the operands, but a batch that breaks the rules above gets
+ *       unspecified values. total may be 0 (then the forward enqueues nothing).
  *
  * Overlap rules: outputs (o, lse; dq, dk, dv, delta) must address every element once
  * (injective strides) and share no element with any input or with each other. Inputs may
@@ -194,6 +203,9 @@ typedef struct {
   int causal;
   float scale;
   int dtype;
+  int N_k;                 /* 0: equal to N */
+  const int* cu_seqlens_k; /* NULL: equal to cu_seqlens */
+  int total_k;             /* with cu_seqlens_k: packed key rows in all */
 } fa_problem;
 
 /* fa_forward() on strided operands / variable-length batches (rules above). */
@@ -206,6 +218,18 @@ int fa_backward_ex(const fa_problem* p, const void* q, fa_strides sq, const void
                    const void* v, fa_strides sv, const void* o, fa_strides so, const void* dO,
                    fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk,
                    fa_strides sdk, void* dv, fa_strides sdv, float* delta, void* stream);
+
+/*
+ * The split-KV forward (fa_forward_splitkv) on a problem of the form above: every Q tile's
+ * key tiles are cut into num_splits ranges. Decode shapes (N = 1, long N_k) fill the GPU
+ * only this way. workspace: device float32 of at least
+ * fa_forward_splitkv_ex_workspace_bytes(p, num_splits) bytes (num_splits * query rows *
+ * (w + 2) * 4, w = the kernel width of d), same rules as for fa_forward_splitkv.
+ */
+int fa_forward_splitkv_ex(const fa_problem* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+                          const void* v, fa_strides sv, void* o, fa_strides so, float* lse, int num_splits,
+                          float* workspace, size_t workspace_bytes, void* stream);
+size_t fa_forward_splitkv_ex_workspace_bytes(const fa_problem* p, int num_splits);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

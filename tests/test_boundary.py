@@ -237,3 +237,61 @@ def test_ex_problem_validation(lib):
     # an empty packed batch validates and enqueues nothing
     assert fwd_ex(lib, p=ex_problem(cu=A[5], total=0)) == fa.FA_OK
     assert bwd_ex(lib, p=ex_problem(cu=A[5], total=0)) == fa.FA_OK
+
+
+def ex_problem_k(N_k=0, cu_k=None, total_k=0, **kw):
+    p = ex_problem(**kw)
+    p.N_k, p.cu_seqlens_k, p.total_k = N_k, cu_k, total_k
+    return p
+
+
+def test_ex_key_side_validation(lib):
+    assert fwd_ex(lib, p=ex_problem_k(N_k=-1)) == fa.FA_ERR_INVALID_ARG
+    assert bwd_ex(lib, p=ex_problem_k(N_k=-1)) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(lib, p=ex_problem_k(N_k=(1 << 30) + 1)) == fa.FA_ERR_UNSUPPORTED
+    # key offsets need query offsets, 16-byte alignment and a non-negative row count
+    assert fwd_ex(lib, p=ex_problem_k(cu_k=A[6], total_k=16)) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(lib, p=ex_problem_k(cu=A[5], total=16, cu_k=A[6] + 4, total_k=16)) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(lib, p=ex_problem_k(cu=A[5], total=16, cu_k=A[6], total_k=-1)) == fa.FA_ERR_INVALID_ARG
+    assert bwd_ex(lib, p=ex_problem_k(cu=A[5], total=16, cu_k=A[6], total_k=-1)) == fa.FA_ERR_INVALID_ARG
+
+
+def test_ex_key_side_extent(lib):
+    # k, v (and dk, dv) span N_k rows: an output placed just past 16 rows of k overlaps a
+    # 1000-row k, and a dk placed there overlaps a 1000-row dv
+    # (one batch, so only the row count decides whether the byte ranges meet)
+    H, N, Nk, d = 2, 16, 1000, 64
+    sq, sk = bnhd(H, N, d), bnhd(H, Nk, d)
+    past_16_rows = A[1] + N * H * d * 2
+    p = ex_problem_k(N_k=Nk, B=1, H=H, N=N, d=d)
+    assert fwd_ex(lib, p=p, ptrs=[A[0], A[1], A[2], past_16_rows], strides=[sq, sk, sk, sq]) == fa.FA_ERR_INVALID_ARG
+    ptrs = list(A)
+    ptrs[7] = A[8] + N * H * d * 2  # dk inside dv
+    assert bwd_ex(lib, p=p, ptrs=ptrs, strides=[sq, sk, sk, sq, sq, sq, sk, sk]) == fa.FA_ERR_INVALID_ARG
+    # a key-side row stride below d is refused like a query-side one
+    assert fwd_ex(lib, p=p, strides=[sq, fa.FAStrides(2048, 64, 32), sk, sq]) == fa.FA_ERR_INVALID_ARG
+
+
+def splitkv_ex(lib, p, splits=2, ws=A[5], ws_bytes=1 << 30):
+    vp = ctypes.c_void_p
+    s = bnhd()
+    return lib.fa_forward_splitkv_ex(ctypes.byref(p), vp(A[0]), s, vp(A[1]), s, vp(A[2]), s, vp(A[3]), s, vp(A[4]),
+                                     splits, vp(ws), ws_bytes, vp(0))
+
+
+def test_splitkv_ex_workspace_and_validation(lib):
+    # bytes: splits * query rows * (kernel width + 2) * 4; query rows are B*H*N, or H*total
+    p = ex_problem_k(N_k=4096, B=2, H=2, N=1, d=64)
+    assert lib.fa_forward_splitkv_ex_workspace_bytes(ctypes.byref(p), 16) == 16 * 2 * 2 * 1 * (64 + 2) * 4
+    p = ex_problem_k(cu=A[5], total=37, cu_k=A[6], total_k=900, N_k=500, B=3, H=2, N=20, d=96)
+    assert lib.fa_forward_splitkv_ex_workspace_bytes(ctypes.byref(p), 3) == 3 * 2 * 37 * (128 + 2) * 4
+    assert lib.fa_forward_splitkv_ex_workspace_bytes(ctypes.byref(p), 0) == 0
+    assert lib.fa_forward_splitkv_ex_workspace_bytes(ctypes.byref(ex_problem_k(N_k=-1)), 2) == 0
+    assert lib.fa_forward_splitkv_ex_workspace_bytes(None, 2) == 0
+    for splits in (0, 257):
+        assert splitkv_ex(lib, ex_problem(), splits=splits) == fa.FA_ERR_INVALID_ARG
+    need = lib.fa_forward_splitkv_ex_workspace_bytes(ctypes.byref(ex_problem()), 2)
+    assert splitkv_ex(lib, ex_problem(), ws_bytes=need - 4) == fa.FA_ERR_INVALID_ARG
+    assert splitkv_ex(lib, ex_problem(), ws=0) == fa.FA_ERR_INVALID_ARG
+    assert splitkv_ex(lib, ex_problem(), ws=A[0]) == fa.FA_ERR_INVALID_ARG  # workspace over q
+    assert splitkv_ex(lib, ex_problem_k(N_k=-1)) == fa.FA_ERR_INVALID_ARG
