@@ -237,6 +237,31 @@ def sweep_extras(fa, FI, torch, np, dev, log):
             _time11(lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, True, dd ** -0.5, stream), torch,
                     np, stream))
         del q, k, v, do, o, lse, delta, dq, dk, dv
+
+    # decode: one new query per sequence against a 4096-key cache (B=8 H=32 d=128 bf16), the
+    # key range cut into 1..64 ranges. Reading the cache (K and V once) bounds it, so it is
+    # reported in GB/s against the HBM peak.
+    Bd, Nk = 8, 4096
+    bits = FI.draw_bits_rect(Bd, H, 1, Nk, d, FI.BF16, 3200)
+    q, k, v = (torch.from_numpy(bits[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(Bd, H, 1, dtype=torch.float32, device=dev)
+    nbytes = 2 * Bd * H * Nk * d * 2 + 2 * Bd * H * d * 2 + Bd * H * 4
+    for splits in (0, 4, 8, 16, 32, 64):
+        if splits == 0:
+            fn = (lambda: fa.fa_forward_ex(q, k, v, o, lse, True, d ** -0.5, "bhnd", stream=stream))
+        else:
+            need = fa.fa_forward_splitkv_ex_workspace_bytes(q, k, splits, "bhnd")
+            ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
+            fn = (lambda s=splits, w=ws: fa.fa_forward_splitkv_ex(q, k, v, o, lse, True, d ** -0.5, s, w, "bhnd",
+                                                                   stream=stream))
+        t = _time11(fn, torch, np, stream)
+        gbs = nbytes / (t["mean_us"] * 1e-6) / 1e9
+        label = f"decode B={Bd} H={H} Nq=1 Nk={Nk} d={d} causal bf16, " + (f"{splits} ranges" if splits else "no split")
+        log(f"  {label:58s} fwd {t['mean_us']:9.1f} us  {gbs:7.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
+        out.append({"extra": label, "fwd": t, "hbm_bytes": nbytes, "gb_per_s": gbs,
+                    "frac_of_hbm_peak": gbs / PEAK_HBM_GBS})
+    del q, k, v, o, lse
     torch.cuda.empty_cache()
     return out
 
