@@ -29,11 +29,14 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "fwd": ["fa_fwd.hip", "fa_common.hpp"],
-    "bwd_preprocess": ["fa_bwd.hip", "fa_common.hpp"],
-    "bwd_dkv": ["fa_bwd_dkv.hip", "fa_common.hpp"],
-    "bwd_dq": ["fa_bwd.hip", "fa_common.hpp"],
+    "fwd": ["fa_fwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
+    "bwd_preprocess": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
+    "bwd_dkv": ["fa_bwd_dkv.hip", "fa_common.hpp", "fa_kernels.hpp"],
+    "bwd_dq": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
 }
+# Kernel-name fragments of each timed kernel in a profiler's per-dispatch records.
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_preprocess": "bwd_preprocess_kernel", "bwd_dkv": "bwd_dkv_kernel",
+                  "bwd_dq": "bwd_dq_kernel"}
 
 
 def log(*a):
@@ -59,6 +62,52 @@ def traffic_for(kernel: str, workload: str):
     if not rec or rec.get("workload") != workload or rec.get("source_sha") != source_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, copy_mib: int, workload: str) -> dict:
+    """HBM bytes per launch of every timed kernel from two rocprofv3 --pmc runs of this script
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same counter read
+    for the plain device copy of copy_mib MiB that --copy-calibration-mib runs last. Writes
+    profiles/traffic.json with the current kernel source hashes and returns the table."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        per = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return per
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copies = [k for k in fetch if "copy" in k.lower()]
+    if len(copies) != 1 or copies[0] not in write:
+        raise SystemExit(f"expected one copy kernel in both counter files, found {copies}")
+    copy_bytes = copy_mib * (1 << 20)
+    f_factor = copy_bytes / (fetch[copies[0]][-1] * 1024)
+    w_factor = copy_bytes / (write[copies[0]][-1] * 1024)
+
+    def find(per, frag):
+        hits = [k for k in per if frag in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {frag}, found {len(hits)}")
+        return per[hits[0]]
+
+    out = {}
+    for name, frag in KERNEL_SYMBOLS.items():
+        fv, wv = find(fetch, frag), find(write, frag)
+        fb = sum(fv) / len(fv) * 1024 * f_factor
+        wb = sum(wv) / len(wv) * 1024 * w_factor
+        out[name] = {"workload": workload, "source_sha": source_sha(name), "bytes_per_launch": round(fb + wb),
+                     "fetch_bytes": round(fb), "write_bytes": round(wb), "fetch_kib_raw": sum(fv) / len(fv),
+                     "write_kib_raw": sum(wv) / len(wv), "dispatches": len(fv)}
+    out["_calibration"] = {"copy_mib": copy_mib, "copy_kernel": copies[0], "fetch_factor": f_factor,
+                           "write_factor": w_factor}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
 
 
 def cpu_baseline(bits, w, heads):
@@ -279,7 +328,16 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling HBM byte counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 --pmc run of this script (with --copy-calibration-mib) into "
+                         "profiles/traffic.json, then exit")
     args = ap.parse_args()
+    if args.ingest_counters:
+        table = ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
+                                args.copy_calibration_mib or 256, args.workload)
+        print(json.dumps(table, indent=1))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
