@@ -7,7 +7,8 @@ against the fp64 oracle on every head, to the tolerances of tests/test_gpu_parit
   * forward and backward through fa_forward_ex / fa_backward_ex for N_q < N_k (down to one
     query) and N_q > N_k (rows that see no key), both masks, d = 64 / 96 / 128 / 256;
   * the split-KV forward on decode shapes (one query, a few thousand keys) and on
-    rectangular ones, every split count giving the same answer;
+    rectangular ones, every split count giving the same answer, and batched decode over
+    ragged key caches (packed sequences of 1-3 queries, one cache empty);
   * packed variable-length batches whose key offsets differ from the query offsets,
     including a sequence with no queries and one with no keys;
   * the autograd wrapper on K and V sliced out of a packed (B, N_k, 2, H, d) tensor.
@@ -240,3 +241,49 @@ def test_autograd_packed_kv(fa):
                 rel = float(np.linalg.norm(got[b, h] - ref[name]) / np.linalg.norm(ref[name]))
                 print(f"{label}: {name}={rel:.3g}", flush=True)
                 assert rel <= TOL_GRAD, (label, name, rel)
+
+
+def test_splitkv_varlen_decode(fa):
+    """Batched decode over ragged key caches: packed sequences of 1-3 queries, each against its
+    own cache length (one empty), through the split-KV forward with separate key offsets."""
+    import torch
+    H, d, dtype = 4, 128, FI.BF16
+    lq = [1, 1, 3, 1, 1, 2]
+    lk = [1, 100, 777, 2048, 0, 3000]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    Tq, Tk = int(cq[-1]), int(ck[-1])
+    bits = FI.draw_bits_rect(1, H, Tq, Tk, d, dtype, 7300)
+    pk = {n: np.ascontiguousarray(bits[n][0].transpose(1, 0, 2)) for n in ("q", "k", "v")}
+    q, k, v = (_lib.to_device(pk[n], dtype) for n in ("q", "k", "v"))
+    cu_q = torch.tensor(cq, dtype=torch.int32, device=q.device)
+    cu_k = torch.tensor(ck, dtype=torch.int32, device=q.device)
+    scale = d ** -0.5
+    kw = dict(cu_seqlens=cu_q, max_seqlen=max(lq), cu_seqlens_k=cu_k, max_seqlen_k=max(lk))
+    for causal in (True, False):
+        refs = {}
+        for b in range(len(lq)):
+            if lk[b] == 0:
+                continue
+            for h in range(H):
+                qf = FI.bits_to_f64(pk["q"][cq[b]:cq[b + 1], h], dtype)
+                kf, vf = (FI.bits_to_f64(pk[n][ck[b]:ck[b + 1], h], dtype) for n in ("k", "v"))
+                refs[b, h] = ORACLE.forward(qf, kf, vf, scale, causal)
+        for splits in (1, 5, 16):
+            o, lse = _nan_like(q), _nan_like(q, (H, Tq))
+            need = fa.fa_forward_splitkv_ex_workspace_bytes(q, k, splits, **kw)
+            assert need == splits * H * Tq * (128 + 2) * 4
+            ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=q.device)
+            fa.fa_forward_splitkv_ex(q, k, v, o, lse, causal, scale, splits, ws, **kw)
+            torch.cuda.synchronize()
+            o_np, lse_np = _lib.from_device(o, dtype), lse.cpu().numpy().astype(np.float64)
+            assert np.all(np.isfinite(o_np)) and not np.any(np.isnan(lse_np))
+            for b in range(len(lq)):
+                rq = slice(cq[b], cq[b + 1])
+                label = f"varlen decode causal={causal} splits={splits} seq{b} (q{lq[b]}, k{lk[b]})"
+                if lk[b] == 0:
+                    assert np.all(o_np[rq] == 0.0) and np.all(lse_np[:, rq] == -np.inf), label
+                    continue
+                for h in range(H):
+                    o_ref, lse_ref = refs[b, h]
+                    compare_head({"o": o_np[rq, h], "lse": lse_np[h, rq]}, {"o": o_ref, "lse": lse_ref}, dtype,
+                                 f"{label} h{h}", grads=False)
