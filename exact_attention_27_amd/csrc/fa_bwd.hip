@@ -21,33 +21,48 @@ namespace fa {
 
 // ------------------------------------------------------------------------------------------
 // [1] D_i = sum_c dO_ic * O_ic, fp32 accumulation, from the stored (rounded) O. A block covers
-// RPB consecutive rows of one statistics head (nrb blocks per head).
+// pre_rows_per_block<D>() consecutive rows of one statistics head (nrb blocks per head): each
+// thread issues the loads of its PASSES rows (16 B of O and of dO each) before using any, so
+// a CU keeps enough bytes in flight to run at the HBM rate rather than at its latency.
+constexpr int kPrePasses = 4;
+template <int D>
+constexpr int pre_rows_per_block() { return kPrePasses * 256 / (D / 8); }
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __restrict__ O,
                                                              const uint16_t* __restrict__ dO,
                                                              float* __restrict__ delta, Geom geo, Strides so,
                                                              Strides sdo, int nrb) {
   constexpr int TPR = D / 8;       // threads per row (16 B each)
-  constexpr int RPB = 256 / TPR;   // rows per block
+  constexpr int RPP = 256 / TPR;   // rows per pass
   const int sub = threadIdx.x % TPR;
   const int hh = blockIdx.x / nrb;
-  const int r = (blockIdx.x - hh * nrb) * RPB + threadIdx.x / TPR;
-  // whole rows (TPR consecutive lanes) leave together, so the shuffles below stay in-row
-  if (r < stat_rows(geo)) {
-    // chunks past the operands' head dim count as zero
-    const bool inside = sub * 8 < geo.dh;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 o = inside ? *reinterpret_cast<const u32x4*>(O + stat_row_offset(geo, so, hh, r) + sub * 8) : z;
-    const u32x4 g = inside ? *reinterpret_cast<const u32x4*>(dO + stat_row_offset(geo, sdo, hh, r) + sub * 8) : z;
+  const int r0 = (blockIdx.x - hh * nrb) * pre_rows_per_block<D>() + threadIdx.x / TPR;
+  const int rows = stat_rows(geo);
+  // chunks past the operands' head dim, and rows past the head, count as zero
+  const bool inside = sub * 8 < geo.dh;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  u32x4 o[kPrePasses], g[kPrePasses];
+#pragma unroll
+  for (int p = 0; p < kPrePasses; ++p) {
+    const int r = r0 + p * RPP;
+    const bool ok = inside && r < rows;
+    o[p] = ok ? *reinterpret_cast<const u32x4*>(O + stat_row_offset(geo, so, hh, r) + sub * 8) : z;
+    g[p] = ok ? *reinterpret_cast<const u32x4*>(dO + stat_row_offset(geo, sdo, hh, r) + sub * 8) : z;
+  }
+#pragma unroll
+  for (int p = 0; p < kPrePasses; ++p) {
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      s = __builtin_fmaf(T::to_f32((uint16_t)(o[w] & 0xffff)), T::to_f32((uint16_t)(g[w] & 0xffff)), s);
-      s = __builtin_fmaf(T::to_f32((uint16_t)(o[w] >> 16)), T::to_f32((uint16_t)(g[w] >> 16)), s);
+      s = __builtin_fmaf(T::to_f32((uint16_t)(o[p][w] & 0xffff)), T::to_f32((uint16_t)(g[p][w] & 0xffff)), s);
+      s = __builtin_fmaf(T::to_f32((uint16_t)(o[p][w] >> 16)), T::to_f32((uint16_t)(g[p][w] >> 16)), s);
     }
+    // every lane takes part (rows past the head reduce zeros), so the shuffles stay in-row
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (sub == 0) delta[(long long)hh * stat_rows(geo) + r] = s;
+    const int r = r0 + p * RPP;
+    if (sub == 0 && r < rows) delta[(long long)hh * rows + r] = s;
   }
 }
 
@@ -318,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
 
 template <typename T, int D>
 static hipError_t launch_pre_t(const BwdArgs& a) {
-  constexpr int RPB = 256 / (D / 8);
+  constexpr int RPB = pre_rows_per_block<D>();
   const int nrb = (stat_rows(a.g) + RPB - 1) / RPB;
   const long long blocks = (long long)stat_heads(a.g) * nrb;
   if (blocks == 0) return hipSuccess;
