@@ -200,11 +200,11 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
       for (int ks = 1; ks < KS; ++ks) s[kb] = T::mfma(kfrag(ktile, kb * KS + ks), qf[ks], s[kb]);
     }
   };
-  // Masking. A key is visible to this lane's row iff key <= key_lim (keys past NK, and with
-  // the causal mask keys after row + off, are hidden; key_lim < 0: the row sees no key). Register i of key block kb holds key
-  // kbase + 4h + kb*32 + 8(i/4) + (i%4), so with thr = key_lim - kbase - 4h an element is
-  // hidden iff the compile-time offset kb*32 + 8(i/4) + (i%4) exceeds thr: one compare and one
-  // select per element.
+  // Masking. A key is visible to this lane's row iff key <= key_lim: keys past NK are hidden,
+  // and with the causal mask so are keys after row + off (key_lim < 0: the row sees no key).
+  // Register i of key block kb holds key kbase + 4h + kb*32 + 8(i/4) + (i%4), so with
+  // thr = key_lim - kbase - 4h an element is hidden iff the compile-time offset
+  // kb*32 + 8(i/4) + (i%4) exceeds thr: one compare and one select per element.
   const int key_lim = CAUSAL ? min(qrow + off, NK - 1) : NK - 1;
   auto mask_thr = [&](int t) { return key_lim - t * BN - 4 * h; };
   auto masked = [](float x, int kb, int i, int thr) {
@@ -217,10 +217,6 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = masked(s[kb][i], kb, i, thr);
   };
-  // Row max of a scores tile -> new reference (moved lazily: only when the tile's max exceeds
-  // the reference by more than kTau; otherwise p = 2^(c s - m_ref) <= 2^kTau accumulates
-  // against the old one). O = acc / l and LSE = ln2 (m_ref + log2 l) hold for any reference
-  // that acc and l share, so skipping a move only skips a rescale of acc.
   // Tile max (this lane's scores) -> new reference, moved lazily: only when the tile's max
   // exceeds the reference by more than kTau; otherwise p = 2^(c s - m_ref) <= 2^kTau
   // accumulates against the old one. O = acc / l and LSE = ln2 (m_ref + log2 l) hold for any
