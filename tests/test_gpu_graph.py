@@ -1,0 +1,109 @@
+"""GPU: forward + backward captured in a HIP graph and replayed.
+
+The library allocates nothing, never synchronises and enqueues only kernels (no memset or
+copy nodes), so a caller can capture a whole attention step on its stream once and replay it.
+Checked here: the graph of fa_forward_ex + fa_backward_ex (strided (B,N,H,d) operands, causal)
+and of fa_forward_splitkv_ex on a decode shape, each replayed several times with the program's
+own eager work and host synchronisations between the replays, with new inputs copied into the
+captured buffers before some replays; every replay must equal an eager run on the same
+inputs bit for bit.
+"""
+import numpy as np
+import pytest
+
+import fa_inputs as FI
+from tests import _lib
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    _lib.ensure_built()
+    import exact_attention_27_amd as fa_mod
+    return fa_mod
+
+
+def _inputs(torch, B, H, Nq, Nk, d, seed):
+    bits = FI.draw_bits_rect(B, H, Nq, Nk, d, FI.BF16, seed)
+    return [_lib.to_device(bits[n], FI.BF16).transpose(1, 2).contiguous() for n in FI.TENSOR_ORDER]
+
+
+def test_graph_forward_backward_replays(fa):
+    import torch
+    B, H, N, d = 2, 4, 700, 128
+    scale = d ** -0.5
+    q, k, v, do = _inputs(torch, B, H, N, N, d, 9100)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.Stream()
+
+    def step(s):
+        fa.fa_forward_ex(q, k, v, o, lse, True, scale, "bnhd", stream=s)
+        fa.fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, True, scale, "bnhd", stream=s)
+
+    def eager_reference():
+        with torch.cuda.stream(stream):
+            step(stream)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (o, lse, dq, dk, dv, delta)]
+
+    ref0 = eager_reference()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    alt = _inputs(torch, B, H, N, N, d, 9101)
+    base = [t.clone() for t in (q, k, v, do)]
+    for replay in range(4):
+        use_alt = replay % 2 == 1
+        for dst, src in zip((q, k, v, do), alt if use_alt else base):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ref = eager_reference() if use_alt else ref0
+        for t in (o, lse, dq, dk, dv, delta):
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("o", "lse", "dq", "dk", "dv", "delta"), (o, lse, dq, dk, dv, delta), ref):
+            assert torch.equal(got.view(torch.int16) if got.dtype != torch.float32 else got.view(torch.int32),
+                               want.view(torch.int16) if want.dtype != torch.float32 else want.view(torch.int32)), \
+                f"replay {replay}: {name} differs from the eager run"
+        print(f"replay {replay} ({'new' if use_alt else 'first'} inputs): bit-identical to eager", flush=True)
+
+
+def test_graph_splitkv_decode_replays(fa):
+    import torch
+    B, H, Nk, d, splits = 4, 8, 3000, 128, 6
+    scale = d ** -0.5
+    q, k, v, _ = _inputs(torch, B, H, 1, Nk, d, 9200)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, 1, dtype=torch.float32, device=q.device)
+    need = fa.fa_forward_splitkv_ex_workspace_bytes(q, k, splits, "bnhd")
+    ws = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        fa.fa_forward_splitkv_ex(q, k, v, o, lse, True, scale, splits, ws, "bnhd", stream=stream)
+    torch.cuda.synchronize()
+    ref = (o.clone(), lse.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fa.fa_forward_splitkv_ex(q, k, v, o, lse, True, scale, splits, ws, "bnhd",
+                                 stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for replay in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16)), f"replay {replay}: o"
+        assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32)), f"replay {replay}: lse"
+        assert np.isfinite(_lib.from_device(o, FI.BF16)).all()
