@@ -99,6 +99,12 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   // sees key j iff j <= i + off).
   const int it_begin = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int it_end = (N + BQ - 1) / BQ;
+  // The steps run downwards, from the end of the sequence to it_begin: every workgroup of a
+  // head then starts on the same query rows at about the same time and they share those
+  // reads in their XCD's L2, where an upward sweep from each tile's own diagonal would have
+  // them at different rows. Steps go in pairs; an odd count starts with one step past N
+  // (it_end), fully masked and reading zeros.
+  const int it_top = it_begin + ((it_end - it_begin + 1) & ~1) - 1;
 
   const int dh = geo.dh;
   if (it_begin >= it_end) {
@@ -120,9 +126,9 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   // At two waves per SIMD registers are short: one lane offset serves all of a wave's copies.
   constexpr bool SHARE = D <= 128;
   stage_rows_swz_buf<D, BK, NW, SHARE>(lds_v, Vh, k0, NK, rsv, dh, wave);
-  stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_q0, Qh, it_begin * BQ, N, rsq, dh, wave);
-  stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_do0, dOh, it_begin * BQ, N, rsdo, dh, wave);
-  if (wave == NW - 1) stage_stats_buf((FA_LDS float*)lds_st0, lse_h, dl_h, it_begin * BQ, N);
+  stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_q0, Qh, it_top * BQ, N, rsq, dh, wave);
+  stage_rows_swz_buf<D, BQ, NW, SHARE>(lds_do0, dOh, it_top * BQ, N, rsdo, dh, wave);
+  if (wave == NW - 1) stage_stats_buf((FA_LDS float*)lds_st0, lse_h, dl_h, it_top * BQ, N);
 
   // Pinned K fragments (B operand of S = Q K^T): lane holds K[key][16ks + 8h .. +7].
   Frag kf[KS];
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     // adds it per read instead of holding KS more loop-invariant addresses)
     int vrow = wave * 32 * D * 2;
     asm volatile("" : "+v"(vrow));
-    const int itn = min(it + 1, it_end - 1);
+    const int itn = max(it - 1, it_begin);  // the next step's tile (clamped: the copy is unconditional)
     const TileSrc rq = tile_src<D, BQ>(Qh, itn * BQ, N, rsq, dh);
     const TileSrc rdo = tile_src<D, BQ>(dOh, itn * BQ, N, rsdo, dh);
     if (wave == NW - 1) stage_stats_buf(stn, lse_h, dl_h, itn * BQ, N);
@@ -291,25 +297,25 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     ring_barrier();
   };
 
-  // Two steps per trip with the slots fixed at compile time. Masked steps: the causal diagonal
-  // (the first BK/BQ steps), and every step when this tile has keys past N; the plain loop
-  // takes the full query tiles after that; the masked tail takes the rest, with one fully
-  // masked padding step (queries past N) when the count is odd.
+  // Two steps per trip (it, then it - 1) with the slots fixed at compile time. Masked steps:
+  // the partial query tile at the top (and the padding step), every step when this tile has
+  // keys past NK, and the causal diagonal at the bottom; the plain loop takes the full query
+  // tiles in between.
   using F = std::false_type;
   using Tr = std::true_type;
   auto pair = [&](auto mask_tag, int it) __attribute__((always_inline)) {
     step(mask_tag, it, lds_q0, lds_do0, lds_st0, lds_q1, lds_do1, (FA_LDS float*)lds_st1);
-    step(mask_tag, it + 1, lds_q1, lds_do1, lds_st1, lds_q0, lds_do0, (FA_LDS float*)lds_st0);
+    step(mask_tag, it - 1, lds_q1, lds_do1, lds_st1, lds_q0, lds_do0, (FA_LDS float*)lds_st0);
   };
   const bool key_tail = k0 + BK > NK;
   // the first step whose rows all see every key of the tile: qbase + off >= k0 + BK - 1
   const int full_from = max(0, k0 + BK - 1 - off);
   const int plain_begin = key_tail ? it_end : (CAUSAL ? min(it_end, max(it_begin, (full_from + BQ - 1) / BQ)) : it_begin);
   const int plain_end = key_tail ? it_end : max(plain_begin, N / BQ);
-  int it = it_begin;
-  for (; it < plain_begin; it += 2) pair(Tr(), it);
-  for (; it + 2 <= plain_end; it += 2) pair(F(), it);
-  for (; it < it_end; it += 2) pair(Tr(), it);
+  int it = it_top;
+  for (; it >= plain_end; it -= 2) pair(Tr(), it);
+  for (; it - 1 >= plain_begin; it -= 2) pair(F(), it);
+  for (; it > it_begin; it -= 2) pair(Tr(), it);
   // No copy may still be landing in LDS when the workgroup retires.
   wait_async();
 
