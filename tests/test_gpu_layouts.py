@@ -304,3 +304,47 @@ def test_malformed_cu_seqlens_stay_inside(fa):
         torch.cuda.synchronize()
         for name, buf in (("o", ob), ("lse", lb), ("dq", dqb), ("dk", dkb), ("dv", dvb), ("delta", db)):
             assert torch.isnan(buf[:G]).all() and torch.isnan(buf[-G:]).all(), (cu_list, name)
+
+
+@pytest.mark.timeout(600)
+def test_varlen_full_size_sampled(fa):
+    """A packed batch of the shape bench.py --sweep times (8 sequences, lengths
+    varlen_lengths(8, 4096, 3001), 22030 tokens, H=32, d=128, causal bf16; values drawn per
+    sequence here), in the same launch configuration: three
+    (sequence, head) pairs against the oracle element by element, forward and backward,
+    including the longest (4096-row) sequence, and on every head of every sequence the
+    invariants sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i."""
+    H, d, dtype, causal = 32, 128, FI.BF16, True
+    lengths = [int(n) for n in FI.varlen_lengths(8, 4096, 3001)]
+    scale = d ** -0.5
+    seqs, packed = draw_varlen(lengths, H, d, dtype, 4900)
+    _, (o, lse, dq, dk, dv, delta) = run_varlen(fa, packed, lengths, dtype, causal, scale)
+    out = {n: _lib.from_device(t, dtype) for n, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv))}
+    lse_np, delta_np = lse.cpu().numpy().astype(np.float64), delta.cpu().numpy().astype(np.float64)
+    for n in out:
+        assert np.all(np.isfinite(out[n])), n
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    longest = int(np.argmax(lengths))
+    for b, h in ((0, 0), (3, 17), (longest, 31)):
+        rows = slice(cu[b], cu[b + 1])
+        q, k, v, do = (FI.bits_to_f64(seqs[b][n][0, h], dtype) for n in FI.TENSOR_ORDER)
+        ref = ORACLE.backward(q, k, v, do, scale, causal)
+        gpu = {"o": out["o"][rows, h], "lse": lse_np[h, rows], "dq": out["dq"][rows, h], "dk": out["dk"][rows, h],
+               "dv": out["dv"][rows, h], "delta": delta_np[h, rows]}
+        m = {"o_gate": float((np.abs(gpu["o"] - ref["o"]) - _lib.half_ulp(gpu["o"], dtype)).max()),
+             "lse": float(np.abs(gpu["lse"] - ref["lse"]).max())}
+        for g in ("dq", "dk", "dv"):
+            m[g] = float(np.linalg.norm(gpu[g] - ref[g]) / np.linalg.norm(ref[g]))
+        norm = np.linalg.norm(do, axis=1) * np.linalg.norm(ref["o"], axis=1) + 1e-30
+        m["delta"] = float((np.abs(gpu["delta"] - ref["delta"]) / norm).max())
+        print(f"varlen full size seq{b} (n={lengths[b]}) h{h}: " + " ".join(f"{k}={x:.3g}" for k, x in m.items()),
+              flush=True)
+        assert m["o_gate"] <= 1e-2 and m["lse"] <= 1e-3 and m["delta"] <= 1e-2, m
+        assert max(m["dq"], m["dk"], m["dv"]) <= 2e-2, m
+    do_all = FI.bits_to_f64(packed["do"], dtype)
+    for b in range(len(lengths)):
+        rows = slice(cu[b], cu[b + 1])
+        dk_b, dv_b = out["dk"][rows], out["dv"][rows]  # (n, H, d)
+        dk_sum = np.abs(dk_b.sum(axis=0)).max() / np.abs(dk_b).sum(axis=0).max()
+        dv_gap = np.abs(dv_b.sum(axis=0) - do_all[rows].sum(axis=0)).max() / np.abs(dv_b).sum(axis=0).max()
+        assert dk_sum <= 1e-2 and dv_gap <= 1e-2, (b, dk_sum, dv_gap)
