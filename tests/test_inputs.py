@@ -61,3 +61,17 @@ def test_workload_table():
     w = FI.WORKLOADS[FI.HEADLINE]
     assert (w.B, w.H, w.N, w.d, w.dtype, w.causal) == (4, 32, 4096, 128, FI.BF16, (True,))
     assert FI.WORKLOADS["long_context"].q_mult == 4.0
+
+
+def test_draw_bits_rect_slices_draw_bits():
+    # queries and keys of different lengths: the first Nq (Nk) rows of one draw over max(Nq, Nk)
+    full = FI.draw_bits((2, 3, 50, 16), FI.BF16, 123)
+    for nq, nk in ((50, 7), (7, 50), (50, 50)):
+        r = FI.draw_bits_rect(2, 3, nq, nk, 16, FI.BF16, 123)
+        assert r["q"].shape == (2, 3, nq, 16) and r["do"].shape == (2, 3, nq, 16)
+        assert r["k"].shape == (2, 3, nk, 16) and r["v"].shape == (2, 3, nk, 16)
+        for n, rows in (("q", nq), ("k", nk), ("v", nk), ("do", nq)):
+            assert np.array_equal(r[n], full[n][:, :, :rows]) and r[n].flags["C_CONTIGUOUS"]
+    a = FI.draw_bits_rect(1, 2, 5, 9, 8, FI.FP16, 7)
+    b = FI.draw_bits_rect(1, 2, 5, 9, 8, FI.FP16, 7)
+    assert all(np.array_equal(a[n], b[n]) for n in FI.TENSOR_ORDER)
