@@ -12,6 +12,15 @@ Workload (default): B=4, H=32, N=4096, d=128, causal, bf16, Q, K, V, dO ~ N(0,1)
 two matmuls of the forward); backward 2.5 F; a step counts 3.5 F.
 
 Prints ONE JSON line on stdout. Progress goes to stderr.
+
+Options beyond the contract (--gpus, --steps, --warmup):
+  --sweep                    also time, as 11 single runs each, every workload (forward,
+                             fa_backward, split-KV forward) and the strided, packed, other
+                             head-dim and decode (one query against a key cache) problems
+  --copy-calibration-mib M   after the timed region, one plain device copy of M MiB: the
+                             kernel of known traffic that scales the HBM byte counters
+  --ingest-counters F W      no GPU work: turn the counter files of a FETCH_SIZE and a
+                             WRITE_SIZE rocprofv3 run into profiles/traffic.json
 """
 from __future__ import annotations
 
