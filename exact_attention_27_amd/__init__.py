@@ -399,7 +399,8 @@ def fa_forward_splitkv_ex(q, k, v, o, lse, causal: bool, scale: float, num_split
                           max_seqlen_k=None) -> None:
     """fa_forward_ex with every Q tile's keys cut into num_splits ranges (decode: one query
     against a long key cache); workspace is a float32 GPU tensor of at least
-    fa_forward_splitkv_ex_workspace_bytes bytes (allocated here when None)."""
+    fa_forward_splitkv_ex_workspace_bytes bytes (allocated here when None). About 256
+    workgroups in all did best on MI355X: num_splits ~ 256 / (B * H * ceil(N / 128))."""
     import torch
     prob, qshape, kshape, sshape, varlen = _ex_problem(q, k, layout, cu_seqlens, max_seqlen, causal, scale,
                                                        cu_seqlens_k, max_seqlen_k)
