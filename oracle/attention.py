@@ -110,6 +110,27 @@ def forward_rows(q, k, v, scale: float, causal: bool, rows):
     return p @ _as_f64(v), _lse(m, l)
 
 
+def dq_rows(q, k, v, do, scale: float, causal: bool, rows):
+    """dQ restricted to the query rows ``rows`` (same definition, fewer rows).
+
+    Row i of dQ = scale * dS_i K needs only row i of S, P and dP ("Triton 05", section
+    "dQ 커널 수식"), so this is the plain definition evaluated for a sample of rows -- for
+    spot checks at lengths where the N x N matrices would not fit in memory.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        s[causal_hidden(rows, q.shape[0], k.shape[0])] = -np.inf
+    p, _, _ = softmax_rows(s)
+    dp = do[rows] @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (ds @ k)
+
+
 def backward(q, k, v, do, scale: float, causal: bool):
     """Exact attention backward for one head.
 

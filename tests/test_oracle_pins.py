@@ -394,6 +394,17 @@ def test_forward_rows_matches_full():
         assert np.array_equal(o[rows], orow) and np.array_equal(lse[rows], lrow)
 
 
+def test_dq_rows_matches_full():
+    # rows of the full backward's dQ, with fewer queries than keys and rows that see no key
+    for nq, nk in ((33, 33), (20, 45), (45, 20)):
+        q, do = _rand(121, nq, 8), _rand(122, nq, 8)
+        k, v = _rand(123, nk, 8), _rand(124, nk, 8)
+        rows = [0, 7, nq - 1]
+        for causal in (False, True):
+            full = A.backward(q, k, v, do, 0.5, causal)["dq"]
+            assert np.allclose(A.dq_rows(q, k, v, do, 0.5, causal, rows), full[rows], rtol=1e-12, atol=1e-14)
+
+
 # ----------------------------------------------------------------------------- mutants
 
 def _mutant_forward(kind):
