@@ -306,6 +306,46 @@ def test_malformed_cu_seqlens_stay_inside(fa):
             assert torch.isnan(buf[:G]).all() and torch.isnan(buf[-G:]).all(), (cu_list, name)
 
 
+def test_malformed_cu_seqlens_k_stay_inside(fa):
+    """The same for the key offsets (cu_seqlens_k, separate from the query offsets): clamped
+    on the device to [0, total_k] with lengths cut to max_seqlen_k, so no write lands outside
+    the operands, through the forward, the backward and the split-KV forward."""
+    import torch
+    H, d, T, Tk, G = 2, 64, 300, 400, 4096
+    bits = FI.draw_bits_rect(1, H, T, Tk, d, FI.BF16, 4800)
+    q, do = (_lib.to_device(bits[n][0].transpose(1, 0, 2), FI.BF16) for n in ("q", "do"))
+    k, v = (_lib.to_device(bits[n][0].transpose(1, 0, 2), FI.BF16) for n in ("k", "v"))
+    cu = torch.tensor([0, 100, 200, 300], dtype=torch.int32, device=q.device)
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((G + n + G,), float("nan"), dtype=dtype, device=q.device)
+        return buf, buf[G:G + n].view(*shape)
+
+    cases = [
+        [0, 300, 150, 400],      # decreasing offsets
+        [0, 150, 9000, 400],     # an offset past total_k
+        [-70, 120, 250, 400],    # a negative offset
+        [0, 10, 20, 400],        # a sequence longer than max_seqlen_k (128)
+    ]
+    for cuk_list in cases:
+        cuk = torch.tensor(cuk_list, dtype=torch.int32, device=q.device)
+        kw = dict(cu_seqlens=cu, max_seqlen=100, cu_seqlens_k=cuk, max_seqlen_k=128)
+        (ob, o), (lb, lse) = guarded((T, H, d), q.dtype), guarded((H, T), torch.float32)
+        (dqb, dq), (db, delta) = guarded((T, H, d), q.dtype), guarded((H, T), torch.float32)
+        (dkb, dk), (dvb, dv) = guarded((Tk, H, d), q.dtype), guarded((Tk, H, d), q.dtype)
+        (o2b, o2), (l2b, lse2) = guarded((T, H, d), q.dtype), guarded((H, T), torch.float32)
+        need = fa.fa_forward_splitkv_ex_workspace_bytes(q, k, 3, **kw)
+        wsb, ws = guarded((need // 4,), torch.float32)
+        fa.fa_forward_ex(q, k, v, o, lse, True, d ** -0.5, **kw)
+        fa.fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, True, d ** -0.5, **kw)
+        fa.fa_forward_splitkv_ex(q, k, v, o2, lse2, True, d ** -0.5, 3, ws, **kw)
+        torch.cuda.synchronize()
+        for name, buf in (("o", ob), ("lse", lb), ("dq", dqb), ("delta", db), ("dk", dkb), ("dv", dvb),
+                          ("o split", o2b), ("lse split", l2b), ("workspace", wsb)):
+            assert torch.isnan(buf[:G]).all() and torch.isnan(buf[-G:]).all(), (cuk_list, name)
+
+
 @pytest.mark.timeout(600)
 def test_varlen_full_size_sampled(fa):
     """A packed batch of the shape bench.py --sweep times (8 sequences, lengths
