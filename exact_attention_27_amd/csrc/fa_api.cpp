@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -354,6 +355,21 @@ int check_bwd(const fa_problem* pp, const void* q, const fa_strides& sq, const v
 
 
 }  // namespace
+
+namespace fa {
+
+bool pair_causal_tiles(long long paired_grid) {
+  static std::atomic<int> cus[64];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n <= 0 || paired_grid >= 2LL * n;
+}
+
+}  // namespace fa
 
 extern "C" {
 

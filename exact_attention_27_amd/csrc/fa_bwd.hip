@@ -83,7 +83,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, Geom geo, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdq,
-    int n_qtiles_max, float scale, float c_log2) {
+    int n_qtiles_max, int pair, float scale, float c_log2) {
   constexpr int KB = BN / 32;  // 32-key blocks per K/V tile
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;
@@ -105,12 +105,15 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // Causal: a workgroup takes the pair of Q tiles (n_qtiles-1-p, p), the heavy one first, so
-  // every workgroup has the same number of K/V tiles; an odd middle tile runs alone. A head's
-  // workgroups run together on one XCD (shared K/V reads in its L2).
+  // Causal: when the grid is large (pair), a workgroup takes the pair of Q tiles
+  // (n_qtiles-1-p, p), the heavy one first, so every workgroup has the same number of K/V
+  // tiles; an odd middle tile runs alone. On a grid too small to fill the CUs twice over, one
+  // tile per workgroup, the heaviest first. A head's workgroups run together on one XCD
+  // (shared K/V reads in its L2).
   // The grid covers the longest sequence; a workgroup past its own sequence's tiles exits.
   const int BH = geo.B * geo.H;
-  const int npairs = CAUSAL ? (n_qtiles_max + 1) / 2 : n_qtiles_max;
+  const bool paired = CAUSAL && pair != 0;
+  const int npairs = paired ? (n_qtiles_max + 1) / 2 : n_qtiles_max;
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
@@ -119,8 +122,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
   const int NK = sq_.nk;  // key rows
   const int off = NK - N;  // causal: query i sees key j iff j <= i + off
   const int n_qtiles = (N + BM - 1) / BM;
-  if (pr >= (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles)) return;
-  const int npass = (CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
+  if (pr >= (paired ? (n_qtiles + 1) / 2 : n_qtiles)) return;
+  const int npass = (paired && n_qtiles - 1 - pr != pr) ? 2 : 1;
   const uint16_t* Qh = seq_base(Q, sq, sq_);
   const uint16_t* Kh = seq_base_k(K, sk, sq_);
   const uint16_t* Vh = seq_base_k(V, sv, sq_);
@@ -347,12 +350,14 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   constexpr int NW = 4, BN = 64;
   constexpr int BM = NW * 32;
   const int n_qtiles = (a.g.N + BM - 1) / BM;
-  const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * a.g.B * a.g.H;
+  const long long BH = (long long)a.g.B * a.g.H;
+  const bool pair = CAUSAL && pair_causal_tiles((long long)((n_qtiles + 1) / 2) * BH);
+  const long long grid = (pair ? (n_qtiles + 1) / 2 : n_qtiles) * BH;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dq, a.g, a.sq, a.sk, a.sv, a.sdo, a.sdq,
-                     n_qtiles, a.scale, a.c_log2);
+                     n_qtiles, pair ? 1 : 0, a.scale, a.c_log2);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, Geom geo, Strides sq, Strides sk, Strides sv,
-    Strides sdo, Strides sdk, Strides sdv, int n_ktiles_max, float scale, float c_log2) {
+    Strides sdo, Strides sdk, Strides sdv, int n_ktiles_max, int pair, float scale, float c_log2) {
   constexpr int BK = NW * 32;
   constexpr int BQ = 32;
   constexpr int KS = D / 16;
@@ -60,13 +60,15 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // Causal: low key tiles see the most queries; a workgroup takes the pair of key tiles
-  // (p, n_ktiles-1-p), the heavy one first, so every workgroup streams the same number of Q
-  // tiles; an odd middle tile runs alone. A head's workgroups run together on one XCD (shared
-  // Q/dO reads in its L2).
+  // Causal: low key tiles see the most queries. When the grid is large (pair), a workgroup
+  // takes the pair of key tiles (p, n_ktiles-1-p), the heavy one first, so every workgroup
+  // streams the same number of Q tiles; an odd middle tile runs alone. On a grid too small to
+  // fill the CUs twice over, one tile per workgroup, the heaviest (p = 0) first. A head's
+  // workgroups run together on one XCD (shared Q/dO reads in its L2).
   // The grid covers the longest sequence; a workgroup past its own sequence's tiles exits.
   const int BH = geo.B * geo.H;
-  const int npairs = CAUSAL ? (n_ktiles_max + 1) / 2 : n_ktiles_max;
+  const bool paired = CAUSAL && pair != 0;
+  const int npairs = paired ? (n_ktiles_max + 1) / 2 : n_ktiles_max;
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
@@ -75,8 +77,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   const int NK = sq_.nk;  // key rows
   const int off = NK - N;  // causal: query i sees key j iff j <= i + off
   const int n_ktiles = (NK + BK - 1) / BK;
-  if (pr >= (CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles)) return;
-  const int npass = (CAUSAL && n_ktiles - 1 - pr != pr) ? 2 : 1;
+  if (pr >= (paired ? (n_ktiles + 1) / 2 : n_ktiles)) return;
+  const int npass = (paired && n_ktiles - 1 - pr != pr) ? 2 : 1;
   const uint16_t* Qh = seq_base(Q, sq, sq_);
   const uint16_t* Kh = seq_base_k(K, sk, sq_);
   const uint16_t* Vh = seq_base_k(V, sv, sq_);
@@ -347,12 +349,14 @@ static hipError_t launch_dkv_t(const BwdArgs& a) {
   constexpr int NW = 4;
   constexpr int BK = NW * 32;
   const int n_ktiles = (a.g.Nk + BK - 1) / BK;
-  const long long grid = (long long)(CAUSAL ? (n_ktiles + 1) / 2 : n_ktiles) * a.g.B * a.g.H;
+  const long long BH = (long long)a.g.B * a.g.H;
+  const bool pair = CAUSAL && pair_causal_tiles((long long)((n_ktiles + 1) / 2) * BH);
+  const long long grid = (pair ? (n_ktiles + 1) / 2 : n_ktiles) * BH;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.g, a.sq, a.sk, a.sv,
-                     a.sdo, a.sdk, a.sdv, n_ktiles, a.scale, a.c_log2);
+                     a.sdo, a.sdk, a.sdv, n_ktiles, pair ? 1 : 0, a.scale, a.c_log2);
   return hipGetLastError();
 }
 

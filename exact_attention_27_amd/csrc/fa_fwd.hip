@@ -50,7 +50,7 @@ template <typename T, int D, int BN, int NW, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, Geom geo, Strides sq, Strides sk, Strides sv, Strides so,
-    int n_qtiles_max, float c_log2, float* __restrict__ part, long long rows_all, int splits) {
+    int n_qtiles_max, int pair, float c_log2, float* __restrict__ part, long long rows_all, int splits) {
   constexpr int BM = NW * 32;  // query rows per workgroup
   constexpr int KS = D / 16;   // k-steps over the head dim
   constexpr int DB = D / 32;   // 32-wide blocks of the head dim
@@ -70,14 +70,17 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // Causal: a workgroup takes the pair of Q tiles (n_qtiles-1-p, p), the heavy one first, so
-  // every workgroup has the same number of K/V tiles (no tail of long-running workgroups at the
-  // end of the grid); an odd middle tile runs alone. A head's workgroups run together on one
+  // Causal, when the grid is large (pair): a workgroup takes the pair of Q tiles
+  // (n_qtiles-1-p, p), the heavy one first, so every workgroup has the same number of K/V tiles
+  // (no tail of long-running workgroups at the end of the grid); an odd middle tile runs alone.
+  // On a grid too small to fill the CUs twice over, one tile per workgroup, the heaviest first:
+  // the longest workgroup is then one heavy tile instead of a heavy and a light one. A head's workgroups run together on one
   // XCD (shared K/V reads in its L2).
   // Split-KV: one workgroup per (head, Q tile, key range), no pairing.
   // The grid covers the longest sequence; a workgroup past its own sequence's tiles exits.
   const int BH = geo.B * geo.H;
-  const int npairs = SPLIT ? n_qtiles_max * splits : (CAUSAL ? (n_qtiles_max + 1) / 2 : n_qtiles_max);
+  const bool paired = !SPLIT && CAUSAL && pair != 0;
+  const int npairs = SPLIT ? n_qtiles_max * splits : (paired ? (n_qtiles_max + 1) / 2 : n_qtiles_max);
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
   const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
@@ -87,14 +90,15 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   const int off = NK - N;  // causal: query i sees key j iff j <= i + off
   const int n_qtiles = (N + BM - 1) / BM;
   const int sp = SPLIT ? pr % splits : 0;  // key range of this workgroup
-  if (SPLIT ? pr / splits >= n_qtiles : pr >= (CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles)) return;
-  const int npass = (!SPLIT && CAUSAL && n_qtiles - 1 - pr != pr) ? 2 : 1;
+  if (SPLIT ? pr / splits >= n_qtiles : pr >= (paired ? (n_qtiles + 1) / 2 : n_qtiles)) return;
+  const int npass = (paired && n_qtiles - 1 - pr != pr) ? 2 : 1;
   const uint16_t* Qh = seq_base(Q, sq, sq_);
   const uint16_t* Kh = seq_base_k(K, sk, sq_);
   const uint16_t* Vh = seq_base_k(V, sv, sq_);
   uint16_t* Oh = seq_base(O, so, sq_);
   const int rsq = (int)sq.r, rsk = (int)sk.r, rsv = (int)sv.r, rso = (int)so.r;
   for (int pass = 0; pass < npass; ++pass) {
+  // (unpaired causal: one tile per workgroup, the heaviest first)
   const int qt = SPLIT ? pr / splits : (CAUSAL ? (pass == 0 ? n_qtiles - 1 - pr : pr) : pr);
   // every wave is done with the previous tile's LDS slots before this tile's copies start
   if (pass > 0) __syncthreads();
@@ -539,17 +543,19 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
     if (grid > 0)
       hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
                          (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, a.c_log2, a.part, rows_all,
-                         a.splits);
+                         (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, 0, a.c_log2, a.part,
+                         rows_all, a.splits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge(a);
   }
-  const long long grid = (long long)(CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles) * BH;
+  const bool pair = CAUSAL && pair_causal_tiles((long long)((n_qtiles + 1) / 2) * BH);
+  const long long grid = (long long)(pair ? (n_qtiles + 1) / 2 : n_qtiles) * BH;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, a.c_log2, nullptr, 0LL, 0);
+                     (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, pair ? 1 : 0, a.c_log2, nullptr,
+                     0LL, 0);
   return hipGetLastError();
 }
 

@@ -70,6 +70,11 @@ struct BwdArgs {
   void* stream;
 };
 
+// Causal grids pair a heavy and a light tile per workgroup, so that every workgroup has the
+// same work, when the paired grid still gives every CU at least two workgroups; smaller grids
+// run one tile per workgroup, heaviest first, which shortens the longest workgroup.
+bool pair_causal_tiles(long long paired_grid);
+
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_dkv(const BwdArgs& a);
