@@ -118,3 +118,18 @@ def test_head_dim_splitkv(fa, d, splits):
         lerr = float(np.abs(lse[0, h].cpu().numpy() - lse_ref).max())
         print(f"split d={d} s={splits} h{h}: o_gate={gate:.3g} lse={lerr:.3g}", flush=True)
         assert gate <= 1e-2 and lerr <= 1e-3
+
+
+@pytest.mark.parametrize("d", [64, 96, 256])
+def test_paired_tiles_many_heads(fa, d):
+    """Many heads make the causal grid large enough for tile pairing (a heavy and a light Q or
+    K tile per workgroup; N = 300 gives an odd middle tile that runs alone), which the other
+    small shapes here do not reach. Sampled heads against the oracle, forward and backward;
+    every head finite."""
+    import torch
+    B, H, N, dtype, causal = 1, 512, 300, FI.BF16, True
+    bits = FI.draw_bits((B, H, N, d), dtype, 5300 + d)
+    scale = d ** -0.5
+    gpu = run_gpu(fa, bits, dtype, causal, scale)
+    for h in (0, 257, 511):
+        check(head_metrics(gpu, bits, dtype, 0, h, scale, causal), f"paired d={d} h{h}")
