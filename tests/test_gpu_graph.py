@@ -110,7 +110,8 @@ def test_graph_splitkv_decode_replays(fa):
 
 
 def test_concurrent_streams(fa):
-    """The library keeps no global state: forward + backward of two independent problems
+    """The library keeps no per-call global state (only a cache of the CU count): forward +
+    backward of two independent problems
     enqueued on two streams at once (different shapes, one causal and one not) give, bit for
     bit, what each gives alone on one stream."""
     import torch
