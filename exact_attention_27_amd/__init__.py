@@ -125,7 +125,25 @@ def _stream_handle(stream, device):
     import torch
     if stream is None:
         stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise ValueError(f"the stream is on {stream.device}, the operands on {device}: all must share one GPU")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _one_device(device, **tensors):
+    """Every given tensor (None skipped) must live on `device`: a kernel reads and writes all
+    its operands from one GPU."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the operands on {device}: all must share one GPU")
+
+
+def _invoke(entry, device, *args):
+    """Call a C entry point with `device` current (the library's launch-shape choices query
+    the current device; the kernels run on the stream's)."""
+    import torch
+    with torch.cuda.device(device):
+        return getattr(load_library(), entry)(*args)
 
 
 def _ptr(t):
@@ -141,8 +159,9 @@ def fa_forward(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None
         _check_bhnd(name, t, q.shape, q.dtype)
     if lse is not None:
         _check_bhnd("lse", lse, (B, H, N), torch.float32)
-    st = load_library().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
-                                   float(scale), _dtype_code(q), _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, o=o, lse=lse)
+    st = _invoke("fa_forward", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                 float(scale), _dtype_code(q), _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_forward")
 
@@ -167,9 +186,10 @@ def fa_forward_splitkv(q, k, v, o, lse, causal: bool, scale: float, num_splits: 
         workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
     if not workspace.is_cuda or workspace.dtype != torch.float32 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous float32 GPU tensor")
-    st = load_library().fa_forward_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                                           int(bool(causal)), float(scale), _dtype_code(q), int(num_splits),
-                                           _ptr(workspace), workspace.numel() * 4, _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, o=o, lse=lse, workspace=workspace)
+    st = _invoke("fa_forward_splitkv", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                 int(bool(causal)), float(scale), _dtype_code(q), int(num_splits), _ptr(workspace),
+                 workspace.numel() * 4, _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_forward_splitkv")
 
@@ -183,9 +203,10 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, causal: bool, scale: flo
         _check_bhnd(name, t, q.shape, q.dtype)
     for name, t in (("lse", lse), ("delta", delta)):
         _check_bhnd(name, t, (B, H, N), torch.float32)
-    st = load_library().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                                    _ptr(dv), _ptr(delta), B, H, N, d, int(bool(causal)), float(scale),
-                                    _dtype_code(q), _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
+    st = _invoke("fa_backward", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                 _ptr(dv), _ptr(delta), B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
+                 _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_backward")
 
@@ -197,8 +218,9 @@ def fa_backward_preprocess(o, do, delta, stream=None) -> None:
     B, H, N, d = o.shape
     _check_bhnd("do", do, o.shape, o.dtype)
     _check_bhnd("delta", delta, (B, H, N), torch.float32)
-    st = load_library().fa_backward_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, H, N, d, _dtype_code(o),
-                                               _stream_handle(stream, o.device))
+    _one_device(o.device, do=do, delta=delta)
+    st = _invoke("fa_backward_preprocess", o.device, _ptr(o), _ptr(do), _ptr(delta), B, H, N, d, _dtype_code(o),
+                 _stream_handle(stream, o.device))
     if st != FA_OK:
         raise FAError(st, "fa_backward_preprocess")
 
@@ -217,9 +239,10 @@ def _check_stage(q, k, v, do, lse, delta, outs):
 def fa_backward_dkv(q, k, v, do, lse, delta, dk, dv, causal: bool, scale: float, stream=None) -> None:
     """Backward stage 2: dK, dV (K/V tile pinned per workgroup)."""
     B, H, N, d = _check_stage(q, k, v, do, lse, delta, (("dk", dk), ("dv", dv)))
-    st = load_library().fa_backward_dkv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk),
-                                        _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
-                                        _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, do=do, lse=lse, delta=delta, dk=dk, dv=dv)
+    st = _invoke("fa_backward_dkv", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk),
+                 _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
+                 _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_backward_dkv")
 
@@ -227,9 +250,9 @@ def fa_backward_dkv(q, k, v, do, lse, delta, dk, dv, causal: bool, scale: float,
 def fa_backward_dq(q, k, v, do, lse, delta, dq, causal: bool, scale: float, stream=None) -> None:
     """Backward stage 3: dQ (Q tile pinned per workgroup)."""
     B, H, N, d = _check_stage(q, k, v, do, lse, delta, (("dq", dq),))
-    st = load_library().fa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
-                                       B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
-                                       _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, do=do, lse=lse, delta=delta, dq=dq)
+    st = _invoke("fa_backward_dq", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+                 B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_backward_dq")
 
@@ -381,8 +404,9 @@ def fa_forward_ex(q, k, v, o, lse, causal: bool, scale: float, layout: str = "bn
            for n, t, sh in (("q", q, qshape), ("k", k, kshape), ("v", v, kshape), ("o", o, qshape))]
     if lse is not None:
         _check_bhnd("lse", lse, sshape, torch.float32)
-    st = load_library().fa_forward_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2], _ptr(o),
-                                      ops[3], _ptr(lse), _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, o=o, lse=lse, cu_seqlens=cu_seqlens, cu_seqlens_k=cu_seqlens_k)
+    st = _invoke("fa_forward_ex", q.device, ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2],
+                 _ptr(o), ops[3], _ptr(lse), _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_forward_ex")
 
@@ -414,9 +438,11 @@ def fa_forward_splitkv_ex(q, k, v, o, lse, causal: bool, scale: float, num_split
         workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=q.device)
     if not workspace.is_cuda or workspace.dtype != torch.float32 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous float32 GPU tensor")
-    st = lib.fa_forward_splitkv_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2], _ptr(o),
-                                   ops[3], _ptr(lse), int(num_splits), _ptr(workspace),
-                                   workspace.numel() * 4, _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, o=o, lse=lse, workspace=workspace, cu_seqlens=cu_seqlens,
+                cu_seqlens_k=cu_seqlens_k)
+    st = _invoke("fa_forward_splitkv_ex", q.device, ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v),
+                 ops[2], _ptr(o), ops[3], _ptr(lse), int(num_splits), _ptr(workspace), workspace.numel() * 4,
+                 _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_forward_splitkv_ex")
 
@@ -433,9 +459,11 @@ def fa_backward_ex(q, k, v, o, do, lse, dq, dk, dv, delta, causal: bool, scale: 
     ops = [_ex_operand(n, t, sh, q.dtype, layout, varlen) for n, t, sh in names]
     for name, t in (("lse", lse), ("delta", delta)):
         _check_bhnd(name, t, sshape, torch.float32)
-    st = load_library().fa_backward_ex(ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2],
-                                       _ptr(o), ops[3], _ptr(do), ops[4], _ptr(lse), _ptr(dq), ops[5], _ptr(dk),
-                                       ops[6], _ptr(dv), ops[7], _ptr(delta), _stream_handle(stream, q.device))
+    _one_device(q.device, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta, cu_seqlens=cu_seqlens,
+                cu_seqlens_k=cu_seqlens_k)
+    st = _invoke("fa_backward_ex", q.device, ctypes.byref(prob), _ptr(q), ops[0], _ptr(k), ops[1], _ptr(v), ops[2],
+                 _ptr(o), ops[3], _ptr(do), ops[4], _ptr(lse), _ptr(dq), ops[5], _ptr(dk), ops[6], _ptr(dv), ops[7],
+                 _ptr(delta), _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_backward_ex")
 

@@ -38,12 +38,16 @@
  *              bottom-right alignment coincide).
  *   Scale      finite and > 0 (1/sqrt(d) for standard attention).
  *   Memory     all pointers are DEVICE pointers owned by the caller, 16-byte aligned.
- *              The library never allocates, frees or retains memory and keeps no
- *              global mutable state: calls are re-entrant. Outputs must not overlap
- *              inputs or each other.
+ *              The library never allocates, frees or retains memory. Its only global
+ *              state is a per-device cache of the CU count, filled on first use with
+ *              atomic stores: calls are re-entrant. Outputs must not overlap inputs or
+ *              each other.
  *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work is
  *              enqueued on it and the call returns without synchronising; buffers
- *              must stay alive until the stream reaches that point.
+ *              must stay alive until the stream reaches that point. Every pointer
+ *              must be memory of the stream's device, and that device must be the
+ *              calling thread's current one. The launch shape depends on the current
+ *              device's CU count.
  *   Errors     arguments are validated on the host before anything is enqueued:
  *              FA_ERR_INVALID_ARG for null/misaligned/overlapping pointers,
  *              non-positive sizes, 64-bit size overflow, unknown dtype, a causal

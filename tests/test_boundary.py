@@ -295,3 +295,18 @@ def test_splitkv_ex_workspace_and_validation(lib):
     assert splitkv_ex(lib, ex_problem(), ws=0) == fa.FA_ERR_INVALID_ARG
     assert splitkv_ex(lib, ex_problem(), ws=A[0]) == fa.FA_ERR_INVALID_ARG  # workspace over q
     assert splitkv_ex(lib, ex_problem_k(N_k=-1)) == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_requires_one_device():
+    """Host logic of the binding: every operand and an explicit stream must sit on q's device
+    (a kernel reads all its operands from one GPU). Checked with CPU tensors and a stand-in
+    stream object; nothing is launched."""
+    import types
+    import torch
+    cuda0 = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="k is on cpu"):
+        fa._one_device(cuda0, k=torch.zeros(1), v=None)
+    fa._one_device(torch.device("cpu"), k=torch.zeros(1), v=None, lse=None)  # all on one device: accepted
+    with pytest.raises(ValueError, match="the stream is on cuda:1"):
+        fa._stream_handle(types.SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0), cuda0)
+    assert fa._stream_handle(types.SimpleNamespace(device=cuda0, cuda_stream=1234), cuda0).value == 1234
