@@ -145,7 +145,22 @@ def cpu_baseline(bits, w, heads):
                    f"same workload: fp64 forward+backward materialising S and P, {dt:.2f} s wall; "
                    f"counted 3.5*F per head as for the GPU"),
         "seconds": dt,
+        "host": _host_info(),
     }
+
+
+def _host_info():
+    """The host the oracle ran on: CPU model, CPUs this process may use, memory."""
+    info = {"affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        with open("/proc/meminfo") as f:
+            kib = next((int(ln.split()[1]) for ln in f if ln.startswith("MemTotal:")), None)
+        info["mem_gib"] = round(kib / 2**20, 1) if kib else None
+    except OSError:  # no /proc: report what is known
+        pass
+    return info
 
 
 def sweep_configs(fa, FI, torch, np, dev, log):
