@@ -70,7 +70,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   const bool paired = CAUSAL && pair != 0;
   const int npairs = paired ? (n_ktiles_max + 1) / 2 : n_ktiles_max;
   const int lid = xcd_local_index(blockIdx.x, BH * npairs);
-  const int bh = __builtin_amdgcn_readfirstlane(lid / npairs);  // wave-uniform (keeps pointers scalar)
+  // wave-uniform (keeps pointers scalar)
+  const int bh = __builtin_amdgcn_readfirstlane(head_of_item(lid / npairs, geo.B, geo.H));
   const int pr = __builtin_amdgcn_readfirstlane(lid % npairs);
   const Seq sq_ = seq_of(geo, bh);
   const int N = sq_.n;    // query rows of this sequence

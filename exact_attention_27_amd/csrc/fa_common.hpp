@@ -214,6 +214,13 @@ __device__ __forceinline__ int xcd_local_index(int bid, int total) {
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// Logical head index (the rank of a head in the order work items are dealt out) to b*H + h,
+// with the batch index running fastest. Each XCD takes a contiguous range of logical heads,
+// so in a packed batch every XCD then holds an equal share of every sequence. With b slowest,
+// an XCD would hold whole sequences, and the one that drew the longest would set the time.
+// A bijection on [0, B*H): every head is still visited exactly once.
+__device__ __forceinline__ int head_of_item(int lbh, int B, int H) { return (lbh % B) * H + lbh / B; }
+
 // Per-lane base offsets into a swizzled tile, from which every fragment address follows by
 // an XOR with a compile-time constant (the swizzle is linear over XOR) plus a constant add:
 //  * row reads at (row0 + l32, chunk 2ks + h): element offset = rows_base(row0) ^ (ks << 4);
