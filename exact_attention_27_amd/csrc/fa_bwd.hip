@@ -341,9 +341,8 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
   const int nrb = (stat_rows(a.g) + RPB - 1) / RPB;
   const long long blocks = (long long)stat_heads(a.g) * nrb;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
-                     (const uint16_t*)a.o, (const uint16_t*)a.dO, a.delta, a.g, a.so, a.sdo, nrb);
-  return hipGetLastError();
+  return launch_kernel(&bwd_preprocess_kernel<T, D>, (unsigned)blocks, 256, a.stream, (const uint16_t*)a.o,
+                       (const uint16_t*)a.dO, a.delta, a.g, a.so, a.sdo, nrb);
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -355,11 +354,10 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   const bool pair = CAUSAL && pair_causal_tiles((long long)((n_qtiles + 1) / 2) * BH);
   const long long grid = (pair ? (n_qtiles + 1) / 2 : n_qtiles) * BH;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dq, a.g, a.sq, a.sk, a.sv, a.sdo, a.sdq,
-                     n_qtiles, pair ? 1 : 0, a.scale, a.c_log2);
-  return hipGetLastError();
+  return launch_kernel(&bwd_dq_kernel<T, D, BN, NW, CAUSAL>, (unsigned)grid, NW * 64, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
+                       (uint16_t*)a.dq, a.g, a.sq, a.sk, a.sv, a.sdo, a.sdq, n_qtiles, pair ? 1 : 0, a.scale,
+                       a.c_log2);
 }
 
 template <typename T>

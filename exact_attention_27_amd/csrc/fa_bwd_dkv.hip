@@ -354,11 +354,10 @@ static hipError_t launch_dkv_t(const BwdArgs& a) {
   const bool pair = CAUSAL && pair_causal_tiles((long long)((n_ktiles + 1) / 2) * BH);
   const long long grid = (pair ? (n_ktiles + 1) / 2 : n_ktiles) * BH;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dO, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.g, a.sq, a.sk, a.sv,
-                     a.sdo, a.sdk, a.sdv, n_ktiles, pair ? 1 : 0, a.scale, a.c_log2);
-  return hipGetLastError();
+  return launch_kernel(&bwd_dkv_kernel<T, D, NW, CAUSAL>, (unsigned)grid, NW * 64, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, a.g, a.sq, a.sk, a.sv, a.sdo, a.sdk, a.sdv, n_ktiles,
+                       pair ? 1 : 0, a.scale, a.c_log2);
 }
 
 #ifndef FA_DKV_WIDE_UNIT

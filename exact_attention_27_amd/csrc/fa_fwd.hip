@@ -232,7 +232,12 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     m_run = moved ? mx : m_run;
     // A row that has seen no visible key keeps m_run = -inf; its reference is 0 then.
     const float ref = (m_run == -INFINITY) ? 0.f : m_run;
-    alpha = __builtin_amdgcn_exp2f(m_ref - ref);  // 1 if kept; finite in every case
+    // Once a row has a finite reference it only rises, so m_ref - ref <= 0 and alpha lies in
+    // [0, 1]. The one exception is the first move away from the placeholder 0, where the
+    // first visible tile's max may lie far below zero: 2^(0 - ref) would overflow to +inf
+    // there and turn acc * alpha and l * alpha (both 0) into NaN. acc and l hold nothing yet
+    // at that point, so any finite factor is exact; clamping the exponent at 0 gives 1.
+    alpha = __builtin_amdgcn_exp2f(fminf(m_ref - ref, 0.f));
     m_ref = ref;
   };
   auto row_max = [&](const f32x16 (&s)[KB]) __attribute__((always_inline)) {
@@ -521,9 +526,8 @@ static hipError_t launch_merge_t(const FwdArgs& a) {
   const int nrb = (stat_rows(a.g) + RPB - 1) / RPB;
   const long long grid = (long long)stat_heads(a.g) * nrb;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)a.stream, a.part,
-                     (uint16_t*)a.o, a.lse, a.g, a.so, rows, nrb, a.splits);
-  return hipGetLastError();
+  return launch_kernel(&merge_kernel<T, D>, (unsigned)grid, 256, a.stream, a.part, (uint16_t*)a.o, a.lse, a.g, a.so,
+                       rows, nrb, a.splits);
 }
 
 static hipError_t launch_merge(const FwdArgs& a) {
@@ -541,23 +545,21 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   if (a.splits > 0) {
     const long long grid = (long long)n_qtiles * a.splits * BH;
     const long long rows_all = (long long)stat_heads(a.g) * stat_rows(a.g);
-    if (grid > 0)
-      hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                         (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, 0, a.c_log2, a.part,
-                         rows_all, a.splits);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (grid > 0) {
+      const hipError_t e = launch_kernel(&fwd_kernel<T, D, BN, NW, CAUSAL, true>, (unsigned)grid, NW * 64, a.stream,
+                                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                                         (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, 0, a.c_log2,
+                                         a.part, rows_all, a.splits);
+      if (e != hipSuccess) return e;
+    }
     return launch_merge(a);
   }
   const bool pair = CAUSAL && pair_causal_tiles((long long)((n_qtiles + 1) / 2) * BH);
   const long long grid = (long long)(pair ? (n_qtiles + 1) / 2 : n_qtiles) * BH;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<T, D, BN, NW, CAUSAL, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.g, a.sq, a.sk, a.sv, a.so, n_qtiles, pair ? 1 : 0, a.c_log2, nullptr,
-                     0LL, 0);
-  return hipGetLastError();
+  return launch_kernel(&fwd_kernel<T, D, BN, NW, CAUSAL, false>, (unsigned)grid, NW * 64, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.g,
+                       a.sq, a.sk, a.sv, a.so, n_qtiles, pair ? 1 : 0, a.c_log2, nullptr, 0LL, 0);
 }
 
 template <typename T>

@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <tuple>
+#include <utility>
+
 namespace fa {
 
 // Element strides of one (B, H, N, d) operand: element (b, h, r, c) sits at
@@ -69,6 +72,24 @@ struct BwdArgs {
   float c_log2;
   void* stream;
 };
+
+// Launch `kern` and return the status of this launch alone. hipLaunchKernel reports the
+// launch's own outcome, where hipGetLastError() after a <<<>>> launch would also return an
+// error left pending on the thread by some earlier, unrelated HIP call. The arguments are
+// converted to the kernel's parameter types first and passed by address.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kern)(KArgs...), unsigned grid, unsigned block, void* stream,
+                                Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count must match the kernel's");
+  std::tuple<KArgs...> vals(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(block), ptrs, 0,
+                         static_cast<hipStream_t>(stream));
+}
 
 // Causal grids pair a heavy and a light tile per workgroup, so that every workgroup has the
 // same work, when the paired grid still gives every CU at least two workgroups; smaller grids

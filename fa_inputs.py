@@ -174,6 +174,72 @@ def edge_shapes() -> Iterator[tuple]:
                     yield (1, 2, N, d, dtype, causal, seed)
 
 
+LOGIT_PATTERNS = ("far_negative", "rising", "dominant_last", "near_tau")
+
+
+def draw_bits_logit_pattern(pattern: str, B: int, H: int, N: int, d: int, dtype: str, seed: int) -> dict:
+    """Inputs whose scaled logits s = Q K^T / sqrt(d) take a chosen shape, for the range
+    limits of the exponential. Safe softmax subtracts the row max so that the result is the
+    same for any shift of a row's logits ("FlashAttentionを1から", section "タイリングを阻む、
+    softmaxという壁"); these recipes put rows where a kernel's running max and its rescale
+    factors are pushed to their limits. The shapes, with e0 the first coordinate:
+
+    * far_negative: Q = -4 + 0.5 z, K = 4 + 0.5 z elementwise, so every logit lies near
+      -16 sqrt(d) (-128 at d = 64, -181 at d = 128), with a spread of about 3: exp of any
+      of them underflows in float32, and a running max that starts at 0 is ~180 too high.
+    * rising: Q = 128 e0 + 0.25 z; K[:, 0] a ramp over the keys, centred on zero, rising by
+      12 logit units per 64 keys (other coordinates z): a row's max rises by 12 (17 in
+      log2 units) on every 64-key tile, so any tiled pass has to move its reference on every
+      tile; at N = 1000 the first keys sit near -94, below the float32 range of exp.
+    * dominant_last: Q = 8 e0 + 0.25 z, K = 0.25 z except the last key, K[N-1, 0] = 40 in
+      logit units: every row that sees the last key is dominated by it (its softmax weight
+      is ~1 and the others' are ~e^-40); the reference jumps by ~40 at the last tile.
+    * near_tau: Q = 8 e0 + 0.05 z, K = 0.25 z, with K[:, 0] a step of 5.4 logit units
+      between the first 64 keys and the rest, centred so that the keys' mean is zero: the
+      later keys exceed the first 64 by 5.4 (just under 8 in log2 units), so a pass that moves
+      its reference only when a tile's max exceeds it by more than 2^8 accumulates
+      probabilities close to 2^8 against the first tile's reference.
+
+    z ~ N(0, 1) from numpy Generator(PCG64(seed)), drawn in the order Q, K, V, dO, each of
+    shape (B, H, N, d); V and dO are z itself. Every tensor is rounded once to `dtype`.
+    Apart from far_negative (whose keys must share a large common part), the keys that a row's
+    softmax weights most differ from each other by more than they share, so that the
+    gradient dQ_i = scale sum_j dS_ij K_j, which cancels any part common to the keys, is not
+    dominated by the rounding of dS against that common part.
+    """
+    if pattern not in LOGIT_PATTERNS:
+        raise ValueError(f"unknown logit pattern {pattern!r}")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    z = {name: rng.standard_normal(size=shape, dtype=np.float64) for name in TENSOR_ORDER}
+    root = float(np.sqrt(d))  # logit = (q . k) / root
+    q, k = z["q"], z["k"]
+    if pattern == "far_negative":
+        q = -4.0 + 0.5 * q
+        k = 4.0 + 0.5 * k
+    elif pattern == "rising":
+        a = 128.0
+        q = 0.25 * q
+        q[..., 0] = a
+        k[..., 0] = (12.0 / 64.0) * (np.arange(N) - (N - 1) / 2.0) * root / a
+    elif pattern == "dominant_last":
+        a = 8.0
+        q = 0.25 * q
+        q[..., 0] = a
+        k = 0.25 * k
+        k[..., N - 1, 0] = 40.0 * root / a
+    else:  # near_tau
+        a = 8.0
+        q = 0.05 * q
+        q[..., 0] = a
+        k = 0.25 * k
+        frac = max(N - 64, 0) / N  # share of keys past the first 64
+        k[..., :64, 0] = -5.4 * frac * root / a
+        k[..., 64:, 0] = 5.4 * (1.0 - frac) * root / a
+    return {"q": round_bits(q, dtype), "k": round_bits(k, dtype), "v": round_bits(z["v"], dtype),
+            "do": round_bits(z["do"], dtype)}
+
+
 def varlen_lengths(n_seq: int, n_max: int, seed: int) -> np.ndarray:
     """A seeded mix of sequence lengths for variable-length batches: n_seq lengths drawn
     uniformly from [n_max // 8, n_max] (numpy PCG64), the last forced to n_max so the

@@ -48,3 +48,11 @@ def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
         ulp = np.maximum(ulp, 2.0 ** -24)
     ulp = np.where(x == 0, 2.0 ** -24 if dtype == FI.FP16 else 2.0 ** -133, ulp)
     return 0.5 * ulp
+
+
+def map_threads(fn, items, workers: int = 8):
+    """[fn(x) for x in items] on a small thread pool (numpy releases the GIL in its matrix
+    products and large elementwise operations, so oracle calls on separate heads overlap)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(workers, len(items)))) as ex:
+        return list(ex.map(fn, items))
