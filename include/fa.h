@@ -53,9 +53,11 @@
  *              non-positive sizes, 64-bit size overflow, unknown dtype, a causal
  *              flag other than 0/1, or a non-finite / non-positive scale;
  *              FA_ERR_UNSUPPORTED for a valid request this build does not implement
- *              (head dim above 256 or not a multiple of 8); FA_ERR_HIP if a kernel launch reports an
- *              error. Faults during execution surface at the caller's next
- *              synchronisation, as usual for HIP.
+ *              (head dim above 256 or not a multiple of 8); FA_ERR_HIP if one of this call's
+ *              kernel launches fails (each launch's own status: an error left pending on the
+ *              thread by an earlier, unrelated HIP call is not reported as this call's).
+ *              Faults during execution surface at the caller's next synchronisation, as
+ *              usual for HIP.
  */
 #ifndef FA_H
 #define FA_H
