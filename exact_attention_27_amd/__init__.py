@@ -32,7 +32,8 @@ FA_ERR_HIP = 3
 
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_splitkv", "fa_forward_splitkv_workspace_bytes", "fa_backward",
                     "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_forward_ex", "fa_backward_ex",
-                    "fa_forward_splitkv_ex", "fa_forward_splitkv_ex_workspace_bytes", "fa_status_string")
+                    "fa_forward_splitkv_ex", "fa_forward_splitkv_ex_workspace_bytes", "fa_backward_noalloc",
+                    "fa_backward_noalloc_max_rows", "fa_status_string")
 
 
 class FAStrides(ctypes.Structure):
@@ -89,6 +90,10 @@ def load_library() -> ctypes.CDLL:
     lib.fa_forward_splitkv_ex.restype = i
     lib.fa_forward_splitkv_ex_workspace_bytes.argtypes = [P, i]
     lib.fa_forward_splitkv_ex_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_backward_noalloc.restype = i
+    lib.fa_backward_noalloc_max_rows.argtypes = []
+    lib.fa_backward_noalloc_max_rows.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -209,6 +214,29 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, causal: bool, scale: flo
                  _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_backward")
+
+
+def fa_backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, causal: bool, scale: float, stream=None) -> None:
+    """fa_backward without the delta workspace: the library keeps it in a device array of
+    fa_backward_noalloc_max_rows() rows per GPU, so the call allocates nothing. Calls that
+    overlap in time on one GPU share that array and must not run concurrently."""
+    import torch
+    _check_bhnd("q", q)
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    _one_device(q.device, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv)
+    st = _invoke("fa_backward_noalloc", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                 _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
+                 _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_backward_noalloc")
+
+
+def fa_backward_noalloc_max_rows() -> int:
+    """Most B*H*N rows fa_backward_noalloc accepts (the size of its device array)."""
+    return int(load_library().fa_backward_noalloc_max_rows())
 
 
 def fa_backward_preprocess(o, do, delta, stream=None) -> None:

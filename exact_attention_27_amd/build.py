@@ -38,6 +38,8 @@ SOURCES = {
     "fa_bwd_dkv.hip": VGPR_FORM,
     # 256-wide dK/dV: more registers than the VGPR form can hold (see the file's header)
     "fa_bwd_dkv_wide.hip": [],
+    # the backward entry point whose workspace is a static device array (no allocation)
+    "fa_noalloc.hip": [],
 }
 
 

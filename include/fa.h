@@ -38,9 +38,11 @@
  *              bottom-right alignment coincide).
  *   Scale      finite and > 0 (1/sqrt(d) for standard attention).
  *   Memory     all pointers are DEVICE pointers owned by the caller, 16-byte aligned.
- *              The library never allocates, frees or retains memory. Its only global
+ *              The library never allocates, frees or retains caller memory. Its global
  *              state is a per-device cache of the CU count, filled on first use with
- *              atomic stores: calls are re-entrant. Outputs must not overlap inputs or
+ *              atomic stores, and, for fa_backward_noalloc only, a fixed device array per
+ *              GPU with its cached address: calls are re-entrant (fa_backward_noalloc calls
+ *              that overlap in time on one GPU excepted). Outputs must not overlap inputs or
  *              each other.
  *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work is
  *              enqueued on it and the call returns without synchronising; buffers
@@ -239,6 +241,26 @@ int fa_forward_splitkv_ex(const fa_problem* p, const void* q, fa_strides sq, con
                           const void* v, fa_strides sv, void* o, fa_strides so, float* lse, int num_splits,
                           float* workspace, size_t workspace_bytes, void* stream);
 size_t fa_forward_splitkv_ex_workspace_bytes(const fa_problem* p, int num_splits);
+
+/*
+ * fa_backward() for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid allocation. The arguments
+ * are those of fa_backward() without `delta`: the per-row vector D_i = rowsum(dO_i * O_i) that
+ * the three kernels pass between them lives in a float32 array the library holds in device
+ * memory, one per GPU for the life of the process, of fa_backward_noalloc_max_rows() rows
+ * (2^22: 16 MiB). The call allocates nothing and makes no allocating library call; outputs and
+ * errors are those of fa_backward() (dq, dk, dv bit-identical to it), plus
+ * FA_ERR_UNSUPPORTED when B*H*N exceeds the array. The array's device address is looked up
+ * once per device, on the first call with that device current (FA_ERR_HIP if the lookup
+ * fails). Every call on one GPU shares its array: calls that overlap in time on one GPU (on
+ * two streams, say) race on it and must be serialised by the caller. Nothing in the array has
+ * to start at zero (each call's first kernel writes every row the other two read).
+ */
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float scale, int dtype,
+                        void* stream);
+size_t fa_backward_noalloc_max_rows(void);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

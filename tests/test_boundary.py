@@ -310,3 +310,19 @@ def test_binding_requires_one_device():
     with pytest.raises(ValueError, match="the stream is on cuda:1"):
         fa._stream_handle(types.SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0), cuda0)
     assert fa._stream_handle(types.SimpleNamespace(device=cuda0, cuda_stream=1234), cuda0).value == 1234
+
+
+def test_noalloc_validation(lib):
+    """fa_backward_noalloc refuses bad arguments before any HIP call: a null pointer, a
+    non-positive size, and B*H*N beyond its device array (FA_ERR_UNSUPPORTED)."""
+    vp = ctypes.c_void_p
+    p = [vp(x) for x in A[:9]]
+    limit = lib.fa_backward_noalloc_max_rows()
+    assert limit == 1 << 22
+    for i in range(9):
+        q = list(p)
+        q[i] = vp(0)
+        assert lib.fa_backward_noalloc(*q, 1, 1, 16, 64, 0, 0.125, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_noalloc(*p, 1, 1, 0, 64, 0, 0.125, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_noalloc(*p, 1, 1, limit + 1, 64, 0, 0.125, 0, vp(0)) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_backward_noalloc(*p, 1 << 16, 1 << 16, 1 << 16, 64, 0, 0.125, 0, vp(0)) == fa.FA_ERR_UNSUPPORTED
