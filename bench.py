@@ -13,10 +13,23 @@ two matmuls of the forward); backward 2.5 F; a step counts 3.5 F.
 
 Prints ONE JSON line on stdout. Progress goes to stderr.
 
+Besides the headline steps, the line carries "configs": every workload (and mask setting),
+each kernel timed as 11 runs on one stream, each bracketed by its own HIP events, enqueued
+back to back, the first discarded: the forward, the three backward stages one by one and one fa_backward call, with
+counted TFLOP/s (GB/s for the preprocess), the fraction of the chip's peak, the clock and
+matrix-core utilisation each kernel ran at (from committed counter runs, when they match the
+current sources) and the fp64 oracle's forward and backward wall times on a sample of heads.
+
 Options beyond the contract (--gpus, --steps, --warmup):
-  --sweep                    also time, as 11 single runs each, every workload (forward,
-                             fa_backward, split-KV forward) and the strided, packed, other
-                             head-dim and decode (one query against a key cache) problems
+  --no-configs               leave out the per-workload records
+  --sweep                    also time the split-KV forward (2 and 4 ranges) on every workload,
+                             and the strided, packed, other head-dim and decode (one query
+                             against a key cache) problems
+  --counter-pass             no timing: launch every workload's four kernels 3 times each in a
+                             fixed order, for a rocprofv3 --pmc run that --ingest-sq reads
+  --ingest-sq CSV            no GPU work: turn the counter_collection.csv of a --counter-pass run
+                             (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA) into
+                             profiles/sq_counters.json
   --copy-calibration-mib M   after the timed region, one plain device copy of M MiB: the
                              kernel of known traffic that scales the HBM byte counters
   --ingest-counters F W      no GPU work: turn the counter files of a FETCH_SIZE and a
@@ -37,6 +50,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
+N_SIMDS = 1024              # 256 CUs x 4 SIMDs
+N_XCDS = 8                  # GRBM_GUI_ACTIVE sums the 8 XCDs' cycle counts
+COUNTER_REPEATS = 3         # launches of each kernel per workload in a --counter-pass run
+STAGES = ("fwd", "bwd_preprocess", "bwd_dkv", "bwd_dq")
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
     "bwd_preprocess": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
@@ -164,78 +182,47 @@ def _host_info():
 
 
 def sweep_configs(fa, FI, torch, np, dev, log):
-    """Every workload (and mask setting): forward alone, one fa_backward call, and the split-KV
-    forward with 2 and 4 key ranges, each timed as 11 runs bracketed by HIP events on one
-    stream, the first discarded; counted FLOPs as above."""
+    """The split-KV forward (fa_forward_splitkv) with 2 and 4 key ranges per Q tile on every
+    workload and mask setting, 11 runs each bracketed by HIP events on one stream, the first
+    discarded (workspaces above 1 GiB are skipped)."""
     out = []
     stream = torch.cuda.current_stream(dev)
     for key, w in FI.WORKLOADS.items():
-        bits = FI.draw_workload(w)
-        tdt = torch.bfloat16 if w.dtype == FI.BF16 else torch.float16
-        q, k, v, do = (torch.from_numpy(bits[n].view(np.int16)).to(dev).view(tdt) for n in FI.TENSOR_ORDER)
-        o = torch.empty_like(q)
-        lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
-        delta = torch.empty_like(lse)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bits, t = _config_tensors(FI, torch, np, dev, w)
         for causal in w.causal:
             F = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if causal else 1.0)
             res = {}
-            for name, fn in (("fwd", lambda: fa.fa_forward(q, k, v, o, lse, causal, w.scale(), stream)),
-                             ("bwd", lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, causal,
-                                                            w.scale(), stream))):
-                ts = []
-                for _ in range(11):
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    fn()
-                    b.record(stream)
-                    torch.cuda.synchronize()
-                    ts.append(a.elapsed_time(b))
-                ts = np.array(ts[1:]) * 1e3  # us
-                res[name] = {"mean_us": float(ts.mean()), "std_us": float(ts.std()), "median_us": float(np.median(ts))}
-            # the split-KV forward (fa_forward_splitkv) with 2 and 4 key ranges per Q tile
             for sp in (2, 4):
                 nb = fa.fa_forward_splitkv_workspace_bytes(w.B, w.H, w.N, w.d, sp)
                 if nb > (1 << 30):
                     continue
                 ws = torch.empty(nb // 4, dtype=torch.float32, device=dev)
-                ts = []
-                for _ in range(11):
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    fa.fa_forward_splitkv(q, k, v, o, lse, causal, w.scale(), sp, ws, stream)
-                    b.record(stream)
-                    torch.cuda.synchronize()
-                    ts.append(a.elapsed_time(b))
-                ts = np.array(ts[1:]) * 1e3
-                res[f"fwd_split{sp}"] = {"mean_us": float(ts.mean()), "std_us": float(ts.std()),
-                                         "median_us": float(np.median(ts))}
+                res[f"fwd_split{sp}"] = _time11(lambda: fa.fa_forward_splitkv(t["q"], t["k"], t["v"], t["o"], t["lse"],
+                                                                               causal, w.scale(), sp, ws, stream),
+                                                torch, np, stream)
+                res[f"fwd_split{sp}"]["tflops"] = F / (res[f"fwd_split{sp}"]["mean_us"] * 1e-6) / 1e12
                 del ws
-            fwd_tf = F / (res["fwd"]["mean_us"] * 1e-6) / 1e12
-            tot_tf = 3.5 * F / ((res["fwd"]["mean_us"] + res["bwd"]["mean_us"]) * 1e-6) / 1e12
-            rec = {"workload": key, "label": w.label, "causal": causal, **res,
-                   "fwd_tflops": fwd_tf, "fwd_bwd_tflops": tot_tf}
-            log(f"  {key:13s} causal={int(causal)}  fwd {res['fwd']['mean_us']:9.1f} us (sd {res['fwd']['std_us']:.1f})"
-                f"  bwd {res['bwd']['mean_us']:9.1f} us (sd {res['bwd']['std_us']:.1f})  fwd {fwd_tf:7.1f} TFLOP/s"
-                f"  fwd+bwd {tot_tf:7.1f} TFLOP/s  split-KV fwd: "
-                + ", ".join(f"{k[9:]} ranges {v['mean_us']:.1f} us" for k, v in res.items() if k.startswith("fwd_split")))
-            out.append(rec)
-        del q, k, v, do, o, lse, delta, dq, dk, dv
+            log(f"  {key:13s} causal={int(causal)}  split-KV fwd: "
+                + ", ".join(f"{k[9:]} ranges {v['mean_us']:.1f} us" for k, v in res.items()))
+            out.append({"workload": key, "label": w.label, "causal": causal, **res})
+        del t, bits
         torch.cuda.empty_cache()
     return out
 
 
 def _time11(fn, torch, np, stream):
-    """11 runs of fn bracketed by HIP events on `stream`, the first discarded (microseconds)."""
-    ts = []
-    for _ in range(11):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    """11 runs of fn, each bracketed by its own pair of HIP events on `stream`, the first
+    discarded (microseconds). The runs are enqueued back to back and the host synchronises once
+    at the end: with a host synchronisation after every run the GPU clock never settles and
+    single launches read 10-20% slower than the same kernels in a training step."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(11)]
+    torch.cuda.synchronize()
+    for a, b in evs:
         a.record(stream)
         fn()
         b.record(stream)
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ts = np.array(ts[1:]) * 1e3
+    torch.cuda.synchronize()
+    ts = np.array([a.elapsed_time(b) for a, b in evs[1:]]) * 1e3
     return {"mean_us": float(ts.mean()), "std_us": float(ts.std()), "median_us": float(np.median(ts))}
 
 
@@ -339,6 +326,218 @@ def sweep_extras(fa, FI, torch, np, dev, log):
     return out
 
 
+def copy_calibration(torch, dev, mib, log):
+    """One plain device copy of `mib` MiB: the kernel of known traffic that scales the HBM byte
+    counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {mib} MiB read + {mib} MiB written")
+    del src, dst
+
+
+def config_list(FI):
+    """(workload key, causal) of every workload and mask setting, in a fixed order."""
+    return [(key, causal) for key, w in FI.WORKLOADS.items() for causal in w.causal]
+
+
+def _config_tensors(FI, torch, np, dev, w):
+    bits = FI.draw_workload(w)
+    tdt = torch.bfloat16 if w.dtype == FI.BF16 else torch.float16
+    q, k, v, do = (torch.from_numpy(bits[n].view(np.int16)).to(dev).view(tdt) for n in FI.TENSOR_ORDER)
+    t = {"q": q, "k": k, "v": v, "do": do, "o": torch.empty_like(q),
+         "lse": torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev),
+         "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v)}
+    t["delta"] = torch.empty_like(t["lse"])
+    return bits, t
+
+
+def _stage_fns(fa, t, causal, scale, stream):
+    """The four kernels of a step, each as one call."""
+    return {
+        "fwd": lambda: fa.fa_forward(t["q"], t["k"], t["v"], t["o"], t["lse"], causal, scale, stream),
+        "bwd_preprocess": lambda: fa.fa_backward_preprocess(t["o"], t["do"], t["delta"], stream),
+        "bwd_dkv": lambda: fa.fa_backward_dkv(t["q"], t["k"], t["v"], t["do"], t["lse"], t["delta"], t["dk"], t["dv"],
+                                              causal, scale, stream),
+        "bwd_dq": lambda: fa.fa_backward_dq(t["q"], t["k"], t["v"], t["do"], t["lse"], t["delta"], t["dq"], causal,
+                                            scale, stream),
+    }
+
+
+def kernel_work(name, w, causal):
+    """Algorithmic work of one launch of a kernel on workload w: (bound, amount, unit, peak).
+    Forward F = 4 B H N^2 d, halved for causal; dK/dV 2F (S, dP, dV, dK); dQ 0.5F (dQ only: its
+    S and dP recomputation is the price of having no atomics and is not counted); the
+    preprocess reads O and dO and writes delta (bytes)."""
+    F = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if causal else 1.0)
+    rows = w.B * w.H * w.N
+    return {
+        "fwd": ("mfma", F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_dkv": ("mfma", 2.0 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_dq": ("mfma", 0.5 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_preprocess": ("hbm", (2 * rows * w.d * 2 + rows * 4) / 1e9, "GB/s", PEAK_HBM_GBS),
+    }[name]
+
+
+def counters_for(kernel: str, key: str, causal: bool):
+    """Clock and matrix-core utilisation of a kernel on a workload, from the committed counter
+    run, or None when absent or taken on other sources."""
+    try:
+        with open(SQ_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = table.get(f"{key}|{int(causal)}|{kernel}")
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return {"clock_ghz": rec["clock_ghz"], "mfma_busy": rec["mfma_busy"],
+            "mfma_issued_per_needed": rec.get("mfma_issued_per_needed"), "counter_run_us": rec["us"]}
+
+
+def oracle_times(bits, w, causal, heads):
+    """The fp64 oracle as it stands, forward alone and forward + backward, on `heads`."""
+    import fa_inputs as FI
+    from oracle import attention as ORACLE
+    tf = tb = 0.0
+    for b, h in heads:
+        q, k, v, do = (FI.bits_to_f64(bits[n][b, h], w.dtype) for n in FI.TENSOR_ORDER)
+        t0 = time.perf_counter()
+        ORACLE.forward(q, k, v, w.scale(), causal)
+        t1 = time.perf_counter()
+        ORACLE.backward(q, k, v, do, w.scale(), causal)
+        t2 = time.perf_counter()
+        tf += t1 - t0
+        tb += t2 - t1
+    F = 4.0 * w.N * w.N * w.d * (0.5 if causal else 1.0) * len(heads)
+    return {"heads": len(heads), "of_heads": w.B * w.H, "fwd_s": tf, "fwd_bwd_s": tb,
+            "bwd_s_derived": tb - tf, "fwd_tflops": F / tf / 1e12, "fwd_bwd_tflops": 3.5 * F / tb / 1e12,
+            "note": "oracle.backward recomputes the forward it needs: bwd_s_derived = fwd_bwd_s - fwd_s"}
+
+
+# heads of each workload the oracle is timed on (about 10 s of host work in all)
+ORACLE_HEADS = {"single_head": 1, "small_causal": 8, "gpt2_medium": 32, "llm_layer": 8, "long_context": 1}
+
+
+def config_records(fa, FI, torch, np, dev, log, with_oracle=True):
+    """Every workload and mask setting: each kernel and one fa_backward call timed as 11 runs
+    bracketed by HIP events on one stream (first discarded), roofline fraction per kernel,
+    counter-derived clock and matrix-core utilisation, and the oracle's wall times."""
+    out = []
+    stream = torch.cuda.current_stream(dev)
+    for key, w in FI.WORKLOADS.items():
+        bits, t = _config_tensors(FI, torch, np, dev, w)
+        for causal in w.causal:
+            fns = _stage_fns(fa, t, causal, w.scale(), stream)
+            fns["fwd"]()  # O and LSE for the backward stages
+            kern = {}
+            for name in STAGES:
+                tm = _time11(fns[name], torch, np, stream)
+                bound, work, unit, peak = kernel_work(name, w, causal)
+                ach = work / (tm["mean_us"] * 1e-6)
+                kern[name] = {**tm, "bound": bound, "achieved": ach, "unit": unit, "frac": ach / peak,
+                              "counters": counters_for(name, key, causal)}
+            bwd = _time11(lambda: fa.fa_backward(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["dq"], t["dk"],
+                                                 t["dv"], t["delta"], causal, w.scale(), stream), torch, np, stream)
+            F = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if causal else 1.0)
+            fwd_us = kern["fwd"]["mean_us"]
+            rec = {"workload": key, "label": w.label, "causal": causal, "counted_fwd_flop": F,
+                   "fwd": {k: kern["fwd"][k] for k in ("mean_us", "std_us", "median_us")}, "bwd": bwd,
+                   "fwd_tflops": F / (fwd_us * 1e-6) / 1e12,
+                   "fwd_frac_of_peak": F / (fwd_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                   "fwd_bwd_tflops": 3.5 * F / ((fwd_us + bwd["mean_us"]) * 1e-6) / 1e12,
+                   "kernels": kern}
+            rec["fwd_bwd_frac_of_peak"] = rec["fwd_bwd_tflops"] / PEAK_BF16_TFLOPS
+            if with_oracle:
+                n = min(ORACLE_HEADS.get(key, 1), w.B * w.H)
+                stride = (w.B * w.H) // n
+                heads = [(i // w.H, i % w.H) for i in range(0, w.B * w.H, stride)][:n]
+                rec["oracle"] = oracle_times(bits, w, causal, heads)
+                rec["oracle"]["cores"] = len(os.sched_getaffinity(0))
+            log(f"  {key:13s} causal={int(causal)}  fwd {fwd_us:8.1f} us  bwd {bwd['mean_us']:8.1f} us  "
+                f"fwd {rec['fwd_tflops']:7.1f} TFLOP/s ({rec['fwd_frac_of_peak']:.1%})  fwd+bwd "
+                f"{rec['fwd_bwd_tflops']:7.1f} ({rec['fwd_bwd_frac_of_peak']:.1%})  "
+                + "  ".join(f"{n}={kern[n]['mean_us']:.1f}us/{kern[n]['frac']:.2f}" for n in STAGES)
+                + (f"  oracle fwd {rec['oracle']['fwd_s']:.2f}s fwd+bwd {rec['oracle']['fwd_bwd_s']:.2f}s"
+                   f" on {rec['oracle']['heads']} head(s)" if with_oracle else ""))
+            out.append(rec)
+        del t, bits
+        torch.cuda.empty_cache()
+    return out
+
+
+def counter_pass(fa, FI, torch, np, dev, log):
+    """For a rocprofv3 --pmc run: every workload and mask setting in config_list order, each of
+    the four kernels launched COUNTER_REPEATS times in STAGES order, nothing else of ours."""
+    stream = torch.cuda.current_stream(dev)
+    for key, w in FI.WORKLOADS.items():
+        bits, t = _config_tensors(FI, torch, np, dev, w)
+        for causal in w.causal:
+            fns = _stage_fns(fa, t, causal, w.scale(), stream)
+            for name in STAGES:
+                for _ in range(COUNTER_REPEATS):
+                    fns[name]()
+            torch.cuda.synchronize()
+            log(f"  counter pass: {key} causal={int(causal)} done")
+        del t, bits
+        torch.cuda.empty_cache()
+
+
+def ingest_sq(csv_path: str) -> dict:
+    """Per (workload, mask, kernel) clock and matrix-core utilisation from the
+    counter_collection.csv of a rocprofv3 --pmc run of --counter-pass, with the dispatches of
+    our four kernels attributed by launch order (config_list x STAGES x COUNTER_REPEATS).
+    clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (1024 SIMDs x GRBM_GUI_ACTIVE / 8); MFMA issued per needed = SQ_INSTS_MFMA / (needed FLOP /
+    32768, one 32x32x16 product; for dQ three times its counted work, since it recomputes S
+    and dP) for the three matrix kernels."""
+    import csv
+    import collections
+    import fa_inputs as FI
+    disp = collections.OrderedDict()
+    frags = {"fwd": "fwd_kernel", "bwd_preprocess": "bwd_preprocess_kernel", "bwd_dkv": "bwd_dkv_kernel",
+             "bwd_dq": "bwd_dq_kernel"}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            stage = next((s for s, fr in frags.items() if f"fa::{fr}<" in name), None)
+            if stage is None:
+                continue
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"stage": stage, "name": name,
+                                                        "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    seq = [disp[k] for k in sorted(disp)]
+    plan = [(key, causal, st) for key, causal in config_list(FI) for st in STAGES for _ in range(COUNTER_REPEATS)]
+    if len(seq) != len(plan):
+        raise SystemExit(f"expected {len(plan)} dispatches of the four kernels, found {len(seq)}")
+    acc = collections.defaultdict(list)
+    for d, (key, causal, st) in zip(seq, plan):
+        if d["stage"] != st:
+            raise SystemExit(f"dispatch order mismatch: expected {st} for {key}, found {d['name'][:60]}")
+        acc[(key, causal, st)].append(d)
+    out = {}
+    for (key, causal, st), ds in acc.items():
+        w = FI.WORKLOADS[key]
+        cyc = [d["GRBM_GUI_ACTIVE"] / N_XCDS for d in ds]
+        rec = {"workload": key, "causal": causal, "kernel": st, "source_sha": source_sha(st),
+               "dispatches": len(ds), "us": sum(d["ns"] for d in ds) / len(ds) / 1e3,
+               "clock_ghz": sum(c / d["ns"] for c, d in zip(cyc, ds)) / len(ds),
+               "mfma_busy": sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (N_SIMDS * c) for c, d in zip(cyc, ds)) / len(ds),
+               "kernel_name": ds[0]["name"].split("(")[0]}
+        bound, work, unit, _ = kernel_work(st, w, causal)
+        if bound == "mfma" and "SQ_INSTS_MFMA" in ds[0]:
+            # products the kernel's algorithm needs: the counted work, and for dQ its S and dP too
+            executed = {"fwd": 1.0, "bwd_dkv": 1.0, "bwd_dq": 3.0}[st]
+            rec["mfma_issued_per_needed"] = (sum(d["SQ_INSTS_MFMA"] for d in ds) / len(ds)) / (work * 1e12 * executed / 32768)
+        out[f"{key}|{int(causal)}|{st}"] = rec
+    with open(SQ_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,8 +546,14 @@ def main():
     ap.add_argument("--workload", default="llm_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128)
+    ap.add_argument("--no-configs", action="store_true", help="leave out the per-workload records")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time forward and fa_backward on every workload (table on stderr, 'sweep' in the line)")
+                    help="also time the split-KV forward on every workload and the strided, packed, other head-dim "
+                         "and decode problems (table on stderr, 'sweep' in the line)")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="no timing: launch every workload's four kernels a fixed number of times (rocprofv3 --pmc)")
+    ap.add_argument("--ingest-sq", metavar="CSV",
+                    help="no GPU work: counter_collection.csv of a --counter-pass run -> profiles/sq_counters.json")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling HBM byte counters)")
@@ -357,6 +562,9 @@ def main():
                          "rocprofv3 --pmc run of this script (with --copy-calibration-mib) into "
                          "profiles/traffic.json, then exit")
     args = ap.parse_args()
+    if args.ingest_sq:
+        print(json.dumps(ingest_sq(args.ingest_sq), indent=1))
+        return
     if args.ingest_counters:
         table = ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
                                 args.copy_calibration_mib or 256, args.workload)
@@ -381,6 +589,11 @@ def main():
     fa.load_library()  # raises if libfa.so was not built: there is no fallback
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
+    if args.counter_pass:
+        counter_pass(fa, FI, torch, np, dev, log)
+        if args.copy_calibration_mib > 0:
+            copy_calibration(torch, dev, args.copy_calibration_mib, log)
+        return
     w = FI.WORKLOADS[args.workload]
     causal = w.causal[0]
     scale = w.scale()
@@ -471,18 +684,16 @@ def main():
                       "traffic": traffic_for(n, w.key)}
 
     if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
-        del src, dst
+        copy_calibration(torch, dev, args.copy_calibration_mib, log)
+
+    configs = None
+    if not args.no_configs:
+        log("every workload (11 runs per kernel, first discarded; oracle on a sample of heads):")
+        configs = config_records(fa, FI, torch, np, dev, log, with_oracle=not args.no_cpu_baseline)
 
     sweep = None
     if args.sweep:
-        log("sweep over the workloads (11 runs each, first discarded):")
+        log("split-KV forward on every workload (11 runs each, first discarded):")
         sweep = sweep_configs(fa, FI, torch, np, dev, log)
         log("strided, variable-length and other head dims (11 runs each, first discarded):")
         sweep += sweep_extras(fa, FI, torch, np, dev, log)
@@ -516,6 +727,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "configs": configs,
         "sweep": sweep,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }

@@ -1,0 +1,81 @@
+"""Host logic of bench.py (no GPU): attribution of counter-run dispatches to workloads and
+kernels, and the clock / matrix-core utilisation arithmetic, on a synthetic rocprofv3 CSV."""
+import csv
+import json
+
+import pytest
+
+import bench
+import fa_inputs as FI
+
+NAMES = {"fwd": "void fa::fwd_kernel<fa::BF16, 128, 64, 4, true, false>(int)",
+         "bwd_preprocess": "void fa::bwd_preprocess_kernel<fa::BF16, 128>(int)",
+         "bwd_dkv": "void fa::bwd_dkv_kernel<fa::BF16, 128, 4, true>(int)",
+         "bwd_dq": "void fa::bwd_dq_kernel<fa::BF16, 128, 64, 4, true>(int)"}
+
+
+def _write_csv(path, order, ns=1_000_000, gui=None, busy=None, extra_first=True):
+    """One row per (dispatch, counter); a foreign kernel (a copy) interleaved first."""
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows, d = [], 1
+    if extra_first:
+        rows.append([d, "__amd_rocclr_copyBuffer", "GRBM_GUI_ACTIVE", 5.0, 0, 10])
+        d += 1
+    for i, stage in enumerate(order):
+        start = 1000 + i * 10 * ns
+        g = gui(i) if gui else 8 * 1.5e9 * ns * 1e-9          # 1.5 GHz on every XCD
+        b = busy(i) if busy else 0.5 * 1024 * (g / 8)          # 50% of 1024 SIMDs
+        for name, val in (("GRBM_GUI_ACTIVE", g), ("SQ_VALU_MFMA_BUSY_CYCLES", b), ("SQ_INSTS_MFMA", 1000.0)):
+            rows.append([d, NAMES[stage], name, val, start, start + ns])
+        d += 1
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(fields)
+        w.writerows(rows)
+
+
+def _plan():
+    return [st for _ in bench.config_list(FI) for st in bench.STAGES for _ in range(bench.COUNTER_REPEATS)]
+
+
+def test_ingest_sq_attributes_by_launch_order(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "sq.json"))
+    path = tmp_path / "c.csv"
+    _write_csv(path, _plan())
+    table = bench.ingest_sq(str(path))
+    assert len(table) == len(bench.config_list(FI)) * len(bench.STAGES)
+    for key, causal in bench.config_list(FI):
+        for st in bench.STAGES:
+            rec = table[f"{key}|{int(causal)}|{st}"]
+            assert rec["dispatches"] == bench.COUNTER_REPEATS
+            assert rec["clock_ghz"] == pytest.approx(1.5)
+            assert rec["mfma_busy"] == pytest.approx(0.5)
+            assert rec["us"] == pytest.approx(1000.0)
+    with open(tmp_path / "sq.json") as f:
+        assert json.load(f).keys() == table.keys()
+    # the committed-table lookup sees the current sources
+    rec = bench.counters_for("fwd", "llm_layer", True)
+    assert rec is not None and rec["clock_ghz"] == pytest.approx(1.5)
+
+
+def test_ingest_sq_refuses_a_wrong_order(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "sq.json"))
+    plan = _plan()
+    plan[0], plan[-1] = plan[-1], plan[0]
+    path = tmp_path / "c.csv"
+    _write_csv(path, plan)
+    with pytest.raises(SystemExit):
+        bench.ingest_sq(str(path))
+    _write_csv(path, _plan()[:-1])
+    with pytest.raises(SystemExit):
+        bench.ingest_sq(str(path))
+
+
+def test_kernel_work_counts():
+    w = FI.WORKLOADS["llm_layer"]
+    F = 4.0 * 4 * 32 * 4096 * 4096 * 128 * 0.5
+    assert bench.kernel_work("fwd", w, True)[1] == pytest.approx(F / 1e12)
+    assert bench.kernel_work("bwd_dkv", w, True)[1] == pytest.approx(2 * F / 1e12)
+    assert bench.kernel_work("bwd_dq", w, True)[1] == pytest.approx(0.5 * F / 1e12)
+    rows = 4 * 32 * 4096
+    assert bench.kernel_work("bwd_preprocess", w, True)[1] == pytest.approx((2 * rows * 128 * 2 + rows * 4) / 1e9)
