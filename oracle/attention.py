@@ -149,34 +149,3 @@ def backward(q, k, v, do, scale: float, causal: bool):
     dk = scale * (ds.T @ q)
     delta = (do * o).sum(axis=1)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}
-
-
-def forward_bhnd(q, k, v, scale: float, causal: bool):
-    """Forward over a (B, H, N, d) batch, one head at a time. Returns O (B,H,N,d), LSE (B,H,N)."""
-    B, H, N, _ = q.shape
-    o = np.empty(q.shape[:3] + (v.shape[3],), dtype=np.float64)
-    lse = np.empty((B, H, N), dtype=np.float64)
-    for b in range(B):
-        for h in range(H):
-            o[b, h], lse[b, h] = forward(q[b, h], k[b, h], v[b, h], scale, causal)
-    return o, lse
-
-
-def backward_bhnd(q, k, v, do, scale: float, causal: bool):
-    """Backward over a (B, H, N, d) batch, one head at a time."""
-    B, H, N, d = q.shape
-    dv_dim = v.shape[3]
-    out = {
-        "o": np.empty((B, H, N, dv_dim)),
-        "lse": np.empty((B, H, N)),
-        "dq": np.empty((B, H, N, d)),
-        "dk": np.empty((B, H, N, d)),
-        "dv": np.empty((B, H, N, dv_dim)),
-        "delta": np.empty((B, H, N)),
-    }
-    for b in range(B):
-        for h in range(H):
-            r = backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
-            for name, arr in r.items():
-                out[name][b, h] = arr
-    return out
