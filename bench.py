@@ -27,13 +27,13 @@ Options beyond the contract (--gpus, --steps, --warmup):
                              against a key cache) problems
   --counter-pass             no timing: launch every workload's four kernels 3 times each in a
                              fixed order, for a rocprofv3 --pmc run that --ingest-sq reads
-  --ingest-sq CSV            no GPU work: turn the counter_collection.csv of a --counter-pass run
-                             (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA) into
-                             profiles/sq_counters.json
+  --ingest-sq SQ [FETCH WRITE]
+                             no GPU work: turn the counter_collection.csv files of --counter-pass
+                             rocprofv3 runs (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES,
+                             SQ_INSTS_MFMA; then FETCH_SIZE, then WRITE_SIZE with the copy
+                             calibration) into profiles/counters.json
   --copy-calibration-mib M   after the timed region, one plain device copy of M MiB: the
                              kernel of known traffic that scales the HBM byte counters
-  --ingest-counters F W      no GPU work: turn the counter files of a FETCH_SIZE and a
-                             WRITE_SIZE rocprofv3 run into profiles/traffic.json
 """
 from __future__ import annotations
 
@@ -49,8 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
+SQ_FILE = os.path.join(ROOT, "profiles", "counters.json")
 N_SIMDS = 1024              # 256 CUs x 4 SIMDs
 N_XCDS = 8                  # GRBM_GUI_ACTIVE sums the 8 XCDs' cycle counts
 COUNTER_REPEATS = 3         # launches of each kernel per workload in a --counter-pass run
@@ -78,63 +77,28 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter runs, or None when absent or stale."""
+def algorithmic_bytes(kernel: str, w) -> float:
+    """HBM bytes a kernel must move once on workload w: its operands read and its outputs
+    written, each exactly once (16-bit tensors of B*H*N*d, float32 rows of B*H*N)."""
+    t, r = w.B * w.H * w.N * w.d * 2, w.B * w.H * w.N * 4
+    return {"fwd": 4 * t + r,                   # Q, K, V in; O, LSE out
+            "bwd_preprocess": 2 * t + r,        # O, dO in; delta out
+            "bwd_dkv": 6 * t + 2 * r,           # Q, K, V, dO, LSE, delta in; dK, dV out
+            "bwd_dq": 5 * t + 2 * r}[kernel]    # Q, K, V, dO, LSE, delta in; dQ out
+
+
+def traffic_for(kernel: str, workload: str, causal: bool = True):
+    """HBM bytes per launch from the committed counter runs, or None when absent or taken on
+    other sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(SQ_FILE) as f:
             table = json.load(f)
     except (OSError, ValueError):
         return None
-    rec = table.get(kernel)
-    if not rec or rec.get("workload") != workload or rec.get("source_sha") != source_sha(kernel):
+    rec = table.get(f"{workload}|{int(causal)}|{kernel}")
+    if not rec or rec.get("source_sha") != source_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
-
-
-def ingest_counters(fetch_csv: str, write_csv: str, copy_mib: int, workload: str) -> dict:
-    """HBM bytes per launch of every timed kernel from two rocprofv3 --pmc runs of this script
-    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same counter read
-    for the plain device copy of copy_mib MiB that --copy-calibration-mib runs last. Writes
-    profiles/traffic.json with the current kernel source hashes and returns the table."""
-    import csv
-    import collections
-
-    def per_kernel(path, counter):
-        per = collections.defaultdict(list)
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] == counter:
-                    per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        return per
-
-    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    copies = [k for k in fetch if "copy" in k.lower()]
-    if len(copies) != 1 or copies[0] not in write:
-        raise SystemExit(f"expected one copy kernel in both counter files, found {copies}")
-    copy_bytes = copy_mib * (1 << 20)
-    f_factor = copy_bytes / (fetch[copies[0]][-1] * 1024)
-    w_factor = copy_bytes / (write[copies[0]][-1] * 1024)
-
-    def find(per, frag):
-        hits = [k for k in per if frag in k]
-        if len(hits) != 1:
-            raise SystemExit(f"expected one kernel matching {frag}, found {len(hits)}")
-        return per[hits[0]]
-
-    out = {}
-    for name, frag in KERNEL_SYMBOLS.items():
-        fv, wv = find(fetch, frag), find(write, frag)
-        fb = sum(fv) / len(fv) * 1024 * f_factor
-        wb = sum(wv) / len(wv) * 1024 * w_factor
-        out[name] = {"workload": workload, "source_sha": source_sha(name), "bytes_per_launch": round(fb + wb),
-                     "fetch_bytes": round(fb), "write_bytes": round(wb), "fetch_kib_raw": sum(fv) / len(fv),
-                     "write_kib_raw": sum(wv) / len(wv), "dispatches": len(fv)}
-    out["_calibration"] = {"copy_mib": copy_mib, "copy_kernel": copies[0], "fetch_factor": f_factor,
-                           "write_factor": w_factor}
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    return out
 
 
 def cpu_baseline(bits, w, heads):
@@ -393,8 +357,9 @@ def counters_for(kernel: str, key: str, causal: bool):
     rec = table.get(f"{key}|{int(causal)}|{kernel}")
     if not rec or rec.get("source_sha") != source_sha(kernel):
         return None
-    return {"clock_ghz": rec["clock_ghz"], "mfma_busy": rec["mfma_busy"],
-            "mfma_issued_per_needed": rec.get("mfma_issued_per_needed"), "counter_run_us": rec["us"]}
+    return {"clock_ghz": rec.get("clock_ghz"), "mfma_busy": rec.get("mfma_busy"),
+            "mfma_issued_per_needed": rec.get("mfma_issued_per_needed"), "counter_run_us": rec.get("us"),
+            "hbm_bytes": rec.get("bytes_per_launch")}
 
 
 def oracle_times(bits, w, causal, heads):
@@ -438,6 +403,7 @@ def config_records(fa, FI, torch, np, dev, log, with_oracle=True):
                 bound, work, unit, peak = kernel_work(name, w, causal)
                 ach = work / (tm["mean_us"] * 1e-6)
                 kern[name] = {**tm, "bound": bound, "achieved": ach, "unit": unit, "frac": ach / peak,
+                              "algorithmic_bytes": algorithmic_bytes(name, w),
                               "counters": counters_for(name, key, causal)}
             bwd = _time11(lambda: fa.fa_backward(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["dq"], t["dk"],
                                                  t["dv"], t["delta"], causal, w.scale(), stream), torch, np, stream)
@@ -485,30 +451,34 @@ def counter_pass(fa, FI, torch, np, dev, log):
         torch.cuda.empty_cache()
 
 
-def ingest_sq(csv_path: str) -> dict:
-    """Per (workload, mask, kernel) clock and matrix-core utilisation from the
-    counter_collection.csv of a rocprofv3 --pmc run of --counter-pass, with the dispatches of
-    our four kernels attributed by launch order (config_list x STAGES x COUNTER_REPEATS).
-    clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
-    (1024 SIMDs x GRBM_GUI_ACTIVE / 8); MFMA issued per needed = SQ_INSTS_MFMA / (needed FLOP /
-    32768, one 32x32x16 product; for dQ three times its counted work, since it recomputes S
-    and dP) for the three matrix kernels."""
+def _dispatches(csv_path: str):
+    """Our four kernels' dispatches of a --counter-pass rocprofv3 run, in launch order: a list of
+    {stage, name, ns, <counter>: value} and the copy kernel's counters (or None)."""
     import csv
     import collections
-    import fa_inputs as FI
     disp = collections.OrderedDict()
+    copy = {}
     frags = {"fwd": "fwd_kernel", "bwd_preprocess": "bwd_preprocess_kernel", "bwd_dkv": "bwd_dkv_kernel",
              "bwd_dq": "bwd_dq_kernel"}
     with open(csv_path) as f:
         for r in csv.DictReader(f):
             name = r["Kernel_Name"]
+            if "copy" in name.lower():
+                copy[r["Counter_Name"]] = float(r["Counter_Value"])
+                continue
             stage = next((s for s, fr in frags.items() if f"fa::{fr}<" in name), None)
             if stage is None:
                 continue
             d = disp.setdefault(int(r["Dispatch_Id"]), {"stage": stage, "name": name,
                                                         "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
             d[r["Counter_Name"]] = float(r["Counter_Value"])
-    seq = [disp[k] for k in sorted(disp)]
+    return [disp[k] for k in sorted(disp)], (copy or None)
+
+
+def _attribute(seq):
+    """Group launch-ordered dispatches by (workload key, causal, stage), checking the order."""
+    import collections
+    import fa_inputs as FI
     plan = [(key, causal, st) for key, causal in config_list(FI) for st in STAGES for _ in range(COUNTER_REPEATS)]
     if len(seq) != len(plan):
         raise SystemExit(f"expected {len(plan)} dispatches of the four kernels, found {len(seq)}")
@@ -517,6 +487,42 @@ def ingest_sq(csv_path: str) -> dict:
         if d["stage"] != st:
             raise SystemExit(f"dispatch order mismatch: expected {st} for {key}, found {d['name'][:60]}")
         acc[(key, causal, st)].append(d)
+    return acc
+
+
+def ingest_traffic(fetch_csv: str, write_csv: str, copy_mib: int, table: dict) -> dict:
+    """Add HBM bytes per launch to `table` (from ingest_sq) from a FETCH_SIZE and a WRITE_SIZE
+    --counter-pass run (KiB per dispatch), each scaled by what the same counter read for the
+    plain copy of copy_mib MiB that the counter pass runs last."""
+    fseq, fcopy = _dispatches(fetch_csv)
+    wseq, wcopy = _dispatches(write_csv)
+    if not fcopy or not wcopy:
+        raise SystemExit("no copy kernel in the counter files (run --counter-pass with --copy-calibration-mib)")
+    nbytes = copy_mib * (1 << 20)
+    ff = nbytes / (fcopy["FETCH_SIZE"] * 1024)
+    wf = nbytes / (wcopy["WRITE_SIZE"] * 1024)
+    fa_, wa_ = _attribute(fseq), _attribute(wseq)
+    for (key, causal, st), ds in fa_.items():
+        rec = table.setdefault(f"{key}|{int(causal)}|{st}", {"workload": key, "causal": causal, "kernel": st,
+                                                             "source_sha": source_sha(st)})
+        fb = sum(d["FETCH_SIZE"] for d in ds) / len(ds) * 1024 * ff
+        wb = sum(d["WRITE_SIZE"] for d in wa_[(key, causal, st)]) / len(ds) * 1024 * wf
+        rec.update({"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)})
+    table["_calibration"] = {"copy_mib": copy_mib, "fetch_factor": ff, "write_factor": wf}
+    return table
+
+
+def ingest_sq(csv_path: str, write: bool = True) -> dict:
+    """Per (workload, mask, kernel) clock and matrix-core utilisation from the
+    counter_collection.csv of a rocprofv3 --pmc run of --counter-pass, with the dispatches of
+    our four kernels attributed by launch order (config_list x STAGES x COUNTER_REPEATS).
+    clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (1024 SIMDs x GRBM_GUI_ACTIVE / 8); MFMA issued per needed = SQ_INSTS_MFMA / (needed FLOP /
+    32768, one 32x32x16 product; for dQ three times its counted work, since it recomputes S
+    and dP) for the three matrix kernels."""
+    import fa_inputs as FI
+    seq, _ = _dispatches(csv_path)
+    acc = _attribute(seq)
     out = {}
     for (key, causal, st), ds in acc.items():
         w = FI.WORKLOADS[key]
@@ -532,9 +538,10 @@ def ingest_sq(csv_path: str) -> dict:
             executed = {"fwd": 1.0, "bwd_dkv": 1.0, "bwd_dq": 3.0}[st]
             rec["mfma_issued_per_needed"] = (sum(d["SQ_INSTS_MFMA"] for d in ds) / len(ds)) / (work * 1e12 * executed / 32768)
         out[f"{key}|{int(causal)}|{st}"] = rec
-    with open(SQ_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
+    if write:
+        with open(SQ_FILE, "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
     return out
 
 
@@ -552,22 +559,21 @@ def main():
                          "and decode problems (table on stderr, 'sweep' in the line)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="no timing: launch every workload's four kernels a fixed number of times (rocprofv3 --pmc)")
-    ap.add_argument("--ingest-sq", metavar="CSV",
-                    help="no GPU work: counter_collection.csv of a --counter-pass run -> profiles/sq_counters.json")
+    ap.add_argument("--ingest-sq", nargs="+", metavar="CSV",
+                    help="no GPU work: counter_collection.csv of an SQ --counter-pass run, optionally followed by "
+                         "those of a FETCH_SIZE and a WRITE_SIZE run (with --copy-calibration-mib) -> "
+                         "profiles/sq_counters.json")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling HBM byte counters)")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
-                         "rocprofv3 --pmc run of this script (with --copy-calibration-mib) into "
-                         "profiles/traffic.json, then exit")
     args = ap.parse_args()
     if args.ingest_sq:
-        print(json.dumps(ingest_sq(args.ingest_sq), indent=1))
-        return
-    if args.ingest_counters:
-        table = ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
-                                args.copy_calibration_mib or 256, args.workload)
+        table = ingest_sq(args.ingest_sq[0], write=len(args.ingest_sq) == 1)
+        if len(args.ingest_sq) == 3:
+            table = ingest_traffic(args.ingest_sq[1], args.ingest_sq[2], args.copy_calibration_mib or 256, table)
+            with open(SQ_FILE, "w") as f:
+                json.dump(table, f, indent=1)
+                f.write("\n")
         print(json.dumps(table, indent=1))
         return
 

@@ -14,7 +14,7 @@ NAMES = {"fwd": "void fa::fwd_kernel<fa::BF16, 128, 64, 4, true, false>(int)",
          "bwd_dq": "void fa::bwd_dq_kernel<fa::BF16, 128, 64, 4, true>(int)"}
 
 
-def _write_csv(path, order, ns=1_000_000, gui=None, busy=None, extra_first=True):
+def _write_csv(path, order, ns=1_000_000, gui=None, busy=None, extra_first=True, counters=None, copy=None):
     """One row per (dispatch, counter); a foreign kernel (a copy) interleaved first."""
     fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
     rows, d = [], 1
@@ -25,9 +25,13 @@ def _write_csv(path, order, ns=1_000_000, gui=None, busy=None, extra_first=True)
         start = 1000 + i * 10 * ns
         g = gui(i) if gui else 8 * 1.5e9 * ns * 1e-9          # 1.5 GHz on every XCD
         b = busy(i) if busy else 0.5 * 1024 * (g / 8)          # 50% of 1024 SIMDs
-        for name, val in (("GRBM_GUI_ACTIVE", g), ("SQ_VALU_MFMA_BUSY_CYCLES", b), ("SQ_INSTS_MFMA", 1000.0)):
+        vals = counters(stage) if counters else (("GRBM_GUI_ACTIVE", g), ("SQ_VALU_MFMA_BUSY_CYCLES", b),
+                                                 ("SQ_INSTS_MFMA", 1000.0))
+        for name, val in vals:
             rows.append([d, NAMES[stage], name, val, start, start + ns])
         d += 1
+    if copy is not None:
+        rows.append([d, "__amd_rocclr_copyBuffer", copy[0], copy[1], 0, 10])
     with open(path, "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(fields)
@@ -79,3 +83,21 @@ def test_kernel_work_counts():
     assert bench.kernel_work("bwd_dq", w, True)[1] == pytest.approx(0.5 * F / 1e12)
     rows = 4 * 32 * 4096
     assert bench.kernel_work("bwd_preprocess", w, True)[1] == pytest.approx((2 * rows * 128 * 2 + rows * 4) / 1e9)
+
+
+def test_ingest_traffic_scales_by_the_copy(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE per dispatch (KiB) scaled by what the same counter read for the
+    copy of known size: a copy of 256 MiB that reads as 64 MiB fetched (factor 4) and 256 MiB
+    written (factor 1)."""
+    monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "c.json"))
+    sq, fe, wr = tmp_path / "sq.csv", tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_csv(sq, _plan())
+    kib = {"fwd": 1000.0, "bwd_preprocess": 2000.0, "bwd_dkv": 3000.0, "bwd_dq": 4000.0}
+    _write_csv(fe, _plan(), counters=lambda st: (("FETCH_SIZE", kib[st]),), copy=("FETCH_SIZE", 64 * 1024.0))
+    _write_csv(wr, _plan(), counters=lambda st: (("WRITE_SIZE", kib[st] / 2),), copy=("WRITE_SIZE", 256 * 1024.0))
+    table = bench.ingest_traffic(str(fe), str(wr), 256, bench.ingest_sq(str(sq), write=False))
+    rec = table["llm_layer|1|bwd_dkv"]
+    assert rec["fetch_bytes"] == 4 * 3000 * 1024 and rec["write_bytes"] == 1500 * 1024
+    assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    assert rec["clock_ghz"] == pytest.approx(1.5)
+    assert table["_calibration"]["fetch_factor"] == pytest.approx(4.0)
