@@ -53,16 +53,19 @@ SQ_FILE = os.path.join(ROOT, "profiles", "counters.json")
 N_SIMDS = 1024              # 256 CUs x 4 SIMDs
 N_XCDS = 8                  # GRBM_GUI_ACTIVE sums the 8 XCDs' cycle counts
 COUNTER_REPEATS = 3         # launches of each kernel per workload in a --counter-pass run
-STAGES = ("fwd", "bwd_preprocess", "bwd_dkv", "bwd_dq")
+# the kernels of a step, plus the forward's two-group ping-pong form (fa_forward_pingpong),
+# timed and counted beside them on every workload
+STAGES = ("fwd", "fwd_pingpong", "bwd_preprocess", "bwd_dkv", "bwd_dq")
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
+    "fwd_pingpong": ["fa_fwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
     "bwd_preprocess": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
     "bwd_dkv": ["fa_bwd_dkv.hip", "fa_common.hpp", "fa_kernels.hpp"],
     "bwd_dq": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
 }
 # Kernel-name fragments of each timed kernel in a profiler's per-dispatch records.
-KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_preprocess": "bwd_preprocess_kernel", "bwd_dkv": "bwd_dkv_kernel",
-                  "bwd_dq": "bwd_dq_kernel"}
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "fwd_pingpong": "fwd_kernel", "bwd_preprocess": "bwd_preprocess_kernel",
+                  "bwd_dkv": "bwd_dkv_kernel", "bwd_dq": "bwd_dq_kernel"}
 
 
 def log(*a):
@@ -82,6 +85,7 @@ def algorithmic_bytes(kernel: str, w) -> float:
     written, each exactly once (16-bit tensors of B*H*N*d, float32 rows of B*H*N)."""
     t, r = w.B * w.H * w.N * w.d * 2, w.B * w.H * w.N * 4
     return {"fwd": 4 * t + r,                   # Q, K, V in; O, LSE out
+            "fwd_pingpong": 4 * t + r,
             "bwd_preprocess": 2 * t + r,        # O, dO in; delta out
             "bwd_dkv": 6 * t + 2 * r,           # Q, K, V, dO, LSE, delta in; dK, dV out
             "bwd_dq": 5 * t + 2 * r}[kernel]    # Q, K, V, dO, LSE, delta in; dQ out
@@ -174,11 +178,19 @@ def sweep_configs(fa, FI, torch, np, dev, log):
     return out
 
 
-def _time11(fn, torch, np, stream):
+def _time11(fn, torch, np, stream, settle_s=0.05):
     """11 runs of fn, each bracketed by its own pair of HIP events on `stream`, the first
     discarded (microseconds). The runs are enqueued back to back and the host synchronises once
     at the end: with a host synchronisation after every run the GPU clock never settles and
-    single launches read 10-20% slower than the same kernels in a training step."""
+    single launches read 10-20% slower than the same kernels in a training step. Before them fn
+    runs back to back for about settle_s seconds, for the same reason: after the host-side
+    set-up between workloads the first milliseconds of work ran up to 20% slower and noisier."""
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    once = max(time.perf_counter() - t0, 1e-6)
+    for _ in range(min(2000, max(1, int(settle_s / once)))):
+        fn()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(11)]
     torch.cuda.synchronize()
     for a, b in evs:
@@ -320,9 +332,11 @@ def _config_tensors(FI, torch, np, dev, w):
 
 
 def _stage_fns(fa, t, causal, scale, stream):
-    """The four kernels of a step, each as one call."""
+    """The four kernels of a step and the ping-pong forward, each as one call."""
     return {
         "fwd": lambda: fa.fa_forward(t["q"], t["k"], t["v"], t["o"], t["lse"], causal, scale, stream),
+        "fwd_pingpong": lambda: fa.fa_forward_pingpong(t["q"], t["k"], t["v"], t["o"], t["lse"], causal, scale,
+                                                       stream),
         "bwd_preprocess": lambda: fa.fa_backward_preprocess(t["o"], t["do"], t["delta"], stream),
         "bwd_dkv": lambda: fa.fa_backward_dkv(t["q"], t["k"], t["v"], t["do"], t["lse"], t["delta"], t["dk"], t["dv"],
                                               causal, scale, stream),
@@ -340,6 +354,7 @@ def kernel_work(name, w, causal):
     rows = w.B * w.H * w.N
     return {
         "fwd": ("mfma", F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "fwd_pingpong": ("mfma", F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
         "bwd_dkv": ("mfma", 2.0 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
         "bwd_dq": ("mfma", 0.5 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
         "bwd_preprocess": ("hbm", (2 * rows * w.d * 2 + rows * 4) / 1e9, "GB/s", PEAK_HBM_GBS),
@@ -436,7 +451,7 @@ def config_records(fa, FI, torch, np, dev, log, with_oracle=True):
 
 def counter_pass(fa, FI, torch, np, dev, log):
     """For a rocprofv3 --pmc run: every workload and mask setting in config_list order, each of
-    the four kernels launched COUNTER_REPEATS times in STAGES order, nothing else of ours."""
+    the kernels of STAGES launched COUNTER_REPEATS times each in that order, nothing else of ours."""
     stream = torch.cuda.current_stream(dev)
     for key, w in FI.WORKLOADS.items():
         bits, t = _config_tensors(FI, torch, np, dev, w)
@@ -452,24 +467,23 @@ def counter_pass(fa, FI, torch, np, dev, log):
 
 
 def _dispatches(csv_path: str):
-    """Our four kernels' dispatches of a --counter-pass rocprofv3 run, in launch order: a list of
-    {stage, name, ns, <counter>: value} and the copy kernel's counters (or None)."""
+    """Our kernels' dispatches of a --counter-pass rocprofv3 run, in launch order: a list of
+    {kernel, name, ns, <counter>: value} (kernel: the KERNEL_SYMBOLS family) and the copy
+    kernel's counters (or None)."""
     import csv
     import collections
     disp = collections.OrderedDict()
     copy = {}
-    frags = {"fwd": "fwd_kernel", "bwd_preprocess": "bwd_preprocess_kernel", "bwd_dkv": "bwd_dkv_kernel",
-             "bwd_dq": "bwd_dq_kernel"}
     with open(csv_path) as f:
         for r in csv.DictReader(f):
             name = r["Kernel_Name"]
             if "copy" in name.lower():
                 copy[r["Counter_Name"]] = float(r["Counter_Value"])
                 continue
-            stage = next((s for s, fr in frags.items() if f"fa::{fr}<" in name), None)
-            if stage is None:
+            fam = next((fr for fr in set(KERNEL_SYMBOLS.values()) if f"fa::{fr}<" in name), None)
+            if fam is None:
                 continue
-            d = disp.setdefault(int(r["Dispatch_Id"]), {"stage": stage, "name": name,
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"kernel": fam, "name": name,
                                                         "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
             d[r["Counter_Name"]] = float(r["Counter_Value"])
     return [disp[k] for k in sorted(disp)], (copy or None)
@@ -481,10 +495,10 @@ def _attribute(seq):
     import fa_inputs as FI
     plan = [(key, causal, st) for key, causal in config_list(FI) for st in STAGES for _ in range(COUNTER_REPEATS)]
     if len(seq) != len(plan):
-        raise SystemExit(f"expected {len(plan)} dispatches of the four kernels, found {len(seq)}")
+        raise SystemExit(f"expected {len(plan)} dispatches of our kernels, found {len(seq)}")
     acc = collections.defaultdict(list)
     for d, (key, causal, st) in zip(seq, plan):
-        if d["stage"] != st:
+        if d["kernel"] != KERNEL_SYMBOLS[st]:
             raise SystemExit(f"dispatch order mismatch: expected {st} for {key}, found {d['name'][:60]}")
         acc[(key, causal, st)].append(d)
     return acc
@@ -515,7 +529,7 @@ def ingest_traffic(fetch_csv: str, write_csv: str, copy_mib: int, table: dict) -
 def ingest_sq(csv_path: str, write: bool = True) -> dict:
     """Per (workload, mask, kernel) clock and matrix-core utilisation from the
     counter_collection.csv of a rocprofv3 --pmc run of --counter-pass, with the dispatches of
-    our four kernels attributed by launch order (config_list x STAGES x COUNTER_REPEATS).
+    our kernels attributed by launch order (config_list x STAGES x COUNTER_REPEATS).
     clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
     (1024 SIMDs x GRBM_GUI_ACTIVE / 8); MFMA issued per needed = SQ_INSTS_MFMA / (needed FLOP /
     32768, one 32x32x16 product; for dQ three times its counted work, since it recomputes S
@@ -535,7 +549,7 @@ def ingest_sq(csv_path: str, write: bool = True) -> dict:
         bound, work, unit, _ = kernel_work(st, w, causal)
         if bound == "mfma" and "SQ_INSTS_MFMA" in ds[0]:
             # products the kernel's algorithm needs: the counted work, and for dQ its S and dP too
-            executed = {"fwd": 1.0, "bwd_dkv": 1.0, "bwd_dq": 3.0}[st]
+            executed = {"fwd": 1.0, "fwd_pingpong": 1.0, "bwd_dkv": 1.0, "bwd_dq": 3.0}[st]
             rec["mfma_issued_per_needed"] = (sum(d["SQ_INSTS_MFMA"] for d in ds) / len(ds)) / (work * 1e12 * executed / 32768)
         out[f"{key}|{int(causal)}|{st}"] = rec
     if write:

@@ -30,7 +30,7 @@ FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
-EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_splitkv", "fa_forward_splitkv_workspace_bytes", "fa_backward",
+EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_pingpong", "fa_forward_splitkv", "fa_forward_splitkv_workspace_bytes", "fa_backward",
                     "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_forward_ex", "fa_backward_ex",
                     "fa_forward_splitkv_ex", "fa_forward_splitkv_ex_workspace_bytes", "fa_backward_noalloc",
                     "fa_backward_noalloc_max_rows", "fa_status_string")
@@ -69,6 +69,8 @@ def load_library() -> ctypes.CDLL:
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_forward.restype = i
+    lib.fa_forward_pingpong.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_forward_pingpong.restype = i
     lib.fa_forward_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
     lib.fa_forward_splitkv.restype = i
     lib.fa_forward_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -169,6 +171,22 @@ def fa_forward(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None
                  float(scale), _dtype_code(q), _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_forward")
+
+
+def fa_forward_pingpong(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """fa_forward with the two-group ping-pong schedule (bit-identical outputs; arguments as fa_forward)."""
+    import torch
+    _check_bhnd("q", q)
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    if lse is not None:
+        _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    _one_device(q.device, k=k, v=v, o=o, lse=lse)
+    st = _invoke("fa_forward_pingpong", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                 int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_pingpong")
 
 
 def fa_forward_splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int) -> int:

@@ -242,7 +242,7 @@ bool nothing_to_do_bwd(const fa_problem& p) { return p.cu_seqlens != nullptr && 
 
 int forward_impl(const fa_problem* pp, const void* q, const fa_strides& sq, const void* k, const fa_strides& sk,
                  const void* v, const fa_strides& sv, void* o, const fa_strides& so, float* lse, int splits,
-                 float* part, size_t part_bytes, void* stream) {
+                 float* part, size_t part_bytes, void* stream, bool pingpong = false) {
   if (!pp) return FA_ERR_INVALID_ARG;
   const fa_problem& p = *pp;
   int st = check_shape(p);
@@ -286,6 +286,7 @@ int forward_impl(const fa_problem* pp, const void* q, const fa_strides& sq, cons
   a.stream = stream;
   a.splits = splits;
   a.part = part;
+  a.pingpong = pingpong;
   return fa::launch_forward(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -393,6 +394,13 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   const fa_problem p = fixed_problem(B, H, N, d, causal, scale, dtype);
   const fa_strides c = contiguous(H, N, d);
   return forward_impl(&p, q, c, k, c, v, c, o, c, lse, 0, nullptr, 0, stream);
+}
+
+int fa_forward_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                        int d, int causal, float scale, int dtype, void* stream) {
+  const fa_problem p = fixed_problem(B, H, N, d, causal, scale, dtype);
+  const fa_strides c = contiguous(H, N, d);
+  return forward_impl(&p, q, c, k, c, v, c, o, c, lse, 0, nullptr, 0, stream, true);
 }
 
 int fa_forward_ex(const fa_problem* p, const void* q, fa_strides sq, const void* k, fa_strides sk, const void* v,

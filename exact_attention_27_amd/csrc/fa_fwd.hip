@@ -29,6 +29,15 @@
 // and the max reduction runs under the P V products. The ring staggers K one tile ahead of
 // V: step t reads K(t+1) and V(t) while the copies of K(t+2) and V(t+1) land in the slots
 // that held K(t) and V(t-1); one barrier per step publishes them.
+//
+// Two-group ping-pong (NW = 8, 128-wide tiles, a separate entry point): the matrix product of
+// one query sub-tile runs while the softmax of another runs ("FlashAttention·FA4·FP4", section
+// "HBM을 아낀 뒤에는 무엇이 기다리는가"; "Triton 05", section "4. H100, B200에서의 추가 기법").
+// A workgroup holds 256 query rows in two groups of four waves; the waves of both groups share
+// the SIMDs pairwise, and group Y runs half a step behind group X, with a workgroup barrier
+// after every half step, so each SIMD pairs one wave's [A] half (exponentials) with the other's
+// [B] half (products). The default four-wave form leaves that pairing to the hardware, which
+// interleaves the waves of two independent workgroups on each SIMD.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -47,7 +56,7 @@ constexpr float kTau = 8.0f;
 // [splits][BH*N][D] accumulators, then [splits][BH*N] maxima, then [splits][BH*N] sums;
 // merge_kernel combines them.
 template <typename T, int D, int BN, int NW, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
+__global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, Geom geo, Strides sq, Strides sk, Strides sv, Strides so,
     int n_qtiles_max, int pair, float c_log2, float* __restrict__ part, long long rows_all, int splits) {
@@ -55,6 +64,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   constexpr int KS = D / 16;   // k-steps over the head dim
   constexpr int DB = D / 32;   // 32-wide blocks of the head dim
   constexpr int KB = BN / 32;  // 32-key blocks per tile
+  constexpr int NE = 16 * KB;  // scores of a tile per lane
   static_assert(KB == 2, "the instruction interleaving below is laid out for 64-key tiles");
 
   // One array per ring slot, every slot index a compile-time constant: the compiler can then
@@ -408,6 +418,108 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
   };
+  // ---- the two halves of a step for the two-group ping-pong (NW == 8): [A] S(t+1) || exp S(t),
+  // [B] O += P(t) V(t) || row max of S(t+1), each half issuing its group's share of one tile:
+  // X copies K(t+2) in [A] and V(t+1) in [B]; Y copies V(t+1) in [A] and K(t+3) in [B].
+  f32x16 sn_pp[KB];
+  auto half_a = [&](auto mask_tag, auto parity_tag, int t, bool grpY) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity_tag)::value;
+    const uint16_t* kcur = P ? lds_k0 : lds_k1;  // K(t+1)
+    uint16_t* kdst = P ? lds_k1 : lds_k0;        // K(t+2) replaces K(t)
+    uint16_t* vdst = P ? lds_v0 : lds_v1;        // V(t+1) replaces V(t-1)
+    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 2, last) * BN, NK, rsk, dh);
+    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, NK, rsv, dh);
+    constexpr int CPW = BN * D * 2 / 1024 / NW;
+    constexpr int NA = KB * KS;
+    constexpr int GAP = NA / CPW;
+    Frag kf[3];
+    auto kread = [&](int i) __attribute__((always_inline)) { return kfrag(kcur, (i % KB) * KS + i / KB); };
+    kf[0] = kread(0);
+    kf[1] = kread(1);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if (i % GAP == 0) {
+        if (grpY)
+          stage_copy<D, BN, NW>(vdst, rv, wave, i / GAP);
+        else
+          stage_copy<D, BN, NW>(kdst, rk, wave, i / GAP);
+      }
+      if (i + 2 < NA) kf[(i + 2) % 3] = kread(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kb = i % KB, ks = i / KB;
+      sn_pp[kb] = T::mfma(kf[i % 3], qf[ks], ks == 0 ? f32x16{} : sn_pp[kb]);
+#pragma unroll
+      for (int e = 0; e < NE / NA; ++e) {
+        const int idx = i * (NE / NA) + e;
+        s[idx / 16][idx % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[idx / 16][idx % 16], c_log2, -m_ref));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(s[kb]));
+    rescale();
+  };
+  auto half_b = [&](auto mask_tag, auto parity_tag, int t, bool grpY) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int P = decltype(parity_tag)::value;
+    const uint16_t* vcur = P ? lds_v1 : lds_v0;  // V(t)
+    uint16_t* kcur_w = P ? lds_k0 : lds_k1;      // K(t+3) replaces K(t+1)
+    uint16_t* vdst = P ? lds_v0 : lds_v1;        // V(t+1) replaces V(t-1)
+    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 3, last) * BN, NK, rsk, dh);
+    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, NK, rsv, dh);
+    constexpr int CPW = BN * D * 2 / 1024 / NW;
+    constexpr int NG = KB * 2;
+    constexpr int NB = DB * NG;
+    constexpr int GAP = NB / CPW;
+    Frag pf[NG];
+    pf[0] = pack_group<T>(s[0], 0);
+    Frag vf[3];
+    auto vread = [&](int j) __attribute__((always_inline)) { return vfrag(vcur, j % DB, j / DB); };
+    vf[0] = vread(0);
+    vf[1] = vread(1);
+    float mx = -INFINITY, rs = 0.f;
+    const int thr = mask_thr(t + 1);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j % GAP == 0) {
+        if (grpY)
+          stage_copy<D, BN, NW>(kcur_w, rk, wave, j / GAP);
+        else
+          stage_copy<D, BN, NW>(vdst, rv, wave, j / GAP);
+      }
+      if (j + 2 < NB) vf[(j + 2) % 3] = vread(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int g = j / DB, db = j % DB;
+      acc[db] = T::mfma(vf[j % 3], pf[g], acc[db]);
+      if (g + 1 < NG) {
+        const int gn = g + 1;
+        constexpr int PPC = DB >= 4 ? 1 : 4 / DB;
+#pragma unroll
+        for (int c = 0; c < PPC; ++c) {
+          const int w = db * PPC + c;
+          if (w < 4) pf[gn].v[w] = T::pack2(s[gn / 2][8 * (gn % 2) + 2 * w], s[gn / 2][8 * (gn % 2) + 2 * w + 1]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < NE / NB; ++e) {
+        const int idx = j * (NE / NB) + e;
+        rs += s[idx / 16][idx % 16];
+        float x = sn_pp[idx / 16][idx % 16];
+        if (MASK) {
+          x = masked(x, idx / 16, idx % 16, thr);
+          sn_pp[idx / 16][idx % 16] = x;
+        }
+        mx = fmaxf(mx, x);
+      }
+      asm volatile("" : "+v"(mx), "+v"(rs));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = __builtin_fmaf(l_run, alpha, rs);
+    update_ref(mx);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = sn_pp[kb];
+  };
+
   // ---- last tile: P and P V only.
   auto drain = [&](auto parity_tag) __attribute__((always_inline)) {
     constexpr int P = decltype(parity_tag)::value;
@@ -423,6 +535,74 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
   using Odd = std::integral_constant<int, 1>;
   // Steps whose next tile needs no mask: t + 1 < n_plain.
   const int plain_steps = max(t0, min(n_plain - 1, last));
+  if constexpr (NW == 8) {
+    // Ping-pong of the two 4-wave groups sharing each SIMD: group Y (waves 4..7) runs half a
+    // step behind group X (waves 0..3), so on every SIMD one wave is in its exponential-heavy
+    // [A] half while the other is in its product-heavy [B] half. Every half-step ends with a
+    // workgroup barrier. In half-step k every wave copies its share of one tile: K(t0 + k/2 + 2)
+    // for even k, V(t0 + (k-1)/2 + 1) for odd k, into the slot the previous half-step freed;
+    // the copies of half-step k must have landed by the end of half-step k+1.
+    constexpr int CPWP = BN * D * 2 / 1024 / NW;  // copies per wave per tile
+    const bool grpY = wave >= 4;
+    auto end_slot = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | CPWP);  // vmcnt(CPWP): the previous half-step's copies landed
+      ring_barrier();
+    };
+    // copies of K(tk) into slot (tk - t0) & 1, or of V(tv) into slot (tv - t0) & 1, spread by the halves
+    auto copy_k = [&](int tk, int c) __attribute__((always_inline)) {
+      const int tt = min(tk, last);
+      const TileSrc r = tile_src<D, BN>(Kh, tt * BN, NK, rsk, dh);
+      if (((tk - t0) & 1) == 0) stage_copy<D, BN, NW>(lds_k0, r, wave, c);
+      else stage_copy<D, BN, NW>(lds_k1, r, wave, c);
+    };
+    auto copy_v = [&](int tv, int c) __attribute__((always_inline)) {
+      const TileSrc r = tile_src<D, BN>(Vh, tv * BN, NK, rsv, dh);
+      if (((tv - t0) & 1) == 0) stage_copy<D, BN, NW>(lds_v0, r, wave, c);
+      else stage_copy<D, BN, NW>(lds_v1, r, wave, c);
+    };
+    if (grpY) {
+      // Y's idle first half-step: its share of K(t0 + 2)
+#pragma unroll
+      for (int c = 0; c < CPWP; ++c) copy_k(t0 + 2, c);
+      end_slot();
+    }
+    int t = t0;
+    auto pp_pair = [&](auto mask_tag, int tt) __attribute__((always_inline)) {
+      half_a(mask_tag, Even(), tt, grpY);
+      end_slot();
+      half_b(mask_tag, Even(), tt, grpY);
+      end_slot();
+      half_a(mask_tag, Odd(), tt + 1, grpY);
+      end_slot();
+      half_b(mask_tag, Odd(), tt + 1, grpY);
+      end_slot();
+    };
+    for (; t + 1 < plain_steps; t += 2) pp_pair(F(), t);
+    for (; t < last; t += 2) {
+      half_a(Tr(), Even(), t, grpY);
+      end_slot();
+      half_b(Tr(), Even(), t, grpY);
+      end_slot();
+      if (t + 1 < last) {
+        half_a(Tr(), Odd(), t + 1, grpY);
+        end_slot();
+        half_b(Tr(), Odd(), t + 1, grpY);
+        end_slot();
+      }
+    }
+    // X pads one half-step with a full wait, so that every copy of V(last) (issued in X's and
+    // Y's previous half-step) has landed; then both groups drain together.
+    if (!grpY) {
+      wait_async();
+      ring_barrier();
+    }
+    if ((last - t0) & 1)
+      drain(Odd());
+    else
+      drain(Even());
+    wait_async();
+    ring_barrier();
+  } else {
   int t = t0;
   for (; t + 1 < plain_steps; t += 2) {
     step(F(), Even(), t);
@@ -436,6 +616,7 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void fwd_kernel(
     drain(Odd());
   else
     drain(Even());
+  }
 
   // ---- epilogue: one division per row, store O and LSE
   const float l_tot = half_swap_sum(l_run);
@@ -539,6 +720,18 @@ static hipError_t launch_merge(const FwdArgs& a) {
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int NW = 4, BN = 64;
+  if constexpr (D == 128) if (a.pingpong && a.splits == 0) {
+    // the two-group ping-pong: 8 waves, 256 query rows per workgroup
+    constexpr int NWP = 8, BMP = NWP * 32;
+    const int nqt = (a.g.N + BMP - 1) / BMP;
+    const int BHp = a.g.B * a.g.H;
+    const bool pairp = CAUSAL && pair_causal_tiles((long long)((nqt + 1) / 2) * BHp * 2);
+    const long long gridp = (long long)(pairp ? (nqt + 1) / 2 : nqt) * BHp;
+    if (gridp == 0) return hipSuccess;
+    return launch_kernel(&fwd_kernel<T, D, BN, NWP, CAUSAL, false>, (unsigned)gridp, NWP * 64, a.stream,
+                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.g,
+                         a.sq, a.sk, a.sv, a.so, nqt, pairp ? 1 : 0, a.c_log2, nullptr, 0LL, 0);
+  }
   constexpr int BM = NW * 32;
   const int n_qtiles = (a.g.N + BM - 1) / BM;
   const int BH = a.g.B * a.g.H;

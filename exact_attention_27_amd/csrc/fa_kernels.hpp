@@ -51,6 +51,7 @@ struct FwdArgs {
   void* stream;
   int splits = 0;         // > 0: split-KV forward with this many key ranges per Q tile
   float* part = nullptr;  // split-KV partial states (see fwd_kernel), splits > 0 only
+  bool pingpong = false;  // the two-group ping-pong schedule (128-wide tiles, splits == 0)
 };
 
 struct BwdArgs {

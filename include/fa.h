@@ -93,6 +93,22 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                void* stream);
 
 /*
+ * fa_forward() with the two-group ping-pong schedule: the matrix product of one query
+ * sub-tile overlaps the softmax of another ("FlashAttention·FA4·FP4", section "HBM을 아낀
+ * 뒤에는 무엇이 기다리는가"; "Triton 05: Flash Attention", section "4. H100, B200에서의 추가
+ * 기법"). For 64 < d <= 128 one workgroup of eight waves holds 256 query rows in two groups
+ * of four, one group half a step behind the other, so each SIMD pairs one wave's
+ * exponentials with the other's products. Other head dims run the schedule of fa_forward().
+ * Arguments, outputs and errors are those of fa_forward(), and the outputs are bit-identical
+ * to it (every row goes through the same operations in the same order). On MI355X it measured
+ * slower than fa_forward() at the shapes tried; it is kept for comparison and for hardware
+ * where the pairing pays.
+ */
+int fa_forward_pingpong(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, int causal, float scale, int dtype,
+                        void* stream);
+
+/*
  * Split-KV forward, for grids that would not fill the GPU (few heads, short sequences):
  * the keys of every 128-row Q tile are cut into `num_splits` contiguous ranges of 64-key
  * tiles, one workgroup each computes the softmax state (max m, sum l, unnormalised output)

@@ -34,9 +34,10 @@ def test_status_strings(lib):
 A = [0x10000 * (i + 1) * 0x1000 for i in range(10)]
 
 
-def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0):
+def fwd(lib, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0,
+        entry="fa_forward"):
     vp = ctypes.c_void_p
-    return lib.fa_forward(vp(q), vp(k), vp(v), vp(o), vp(lse), B, H, N, d, causal, scale, dtype, vp(0))
+    return getattr(lib, entry)(vp(q), vp(k), vp(v), vp(o), vp(lse), B, H, N, d, causal, scale, dtype, vp(0))
 
 
 def bwd(lib, ptrs=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0):
@@ -69,6 +70,8 @@ def bwd(lib, ptrs=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=0):
 ])
 def test_forward_validation(lib, kw, code):
     assert fwd(lib, **kw) == code
+    # the ping-pong forward takes the same arguments and validates them the same way
+    assert fwd(lib, entry="fa_forward_pingpong", **{**kw, "d": kw.get("d", 128)}) == code
 
 
 def test_backward_validation(lib):
