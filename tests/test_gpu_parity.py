@@ -1,10 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded bits.
 
 Tolerances (fixed before any GPU result was seen):
-  O      max over elements of (|O_gpu - O_ref| - half_ulp(O_gpu)) <= 1e-2. The raw max|dO| is
-         printed too. Subtracting half an ulp removes the one unavoidable error -- rounding the
-         exact result to the 16-bit storage type -- which alone reaches 0.0078 (bf16, |O| in
-         [2, 4)) and 0.0156 (|O| in [4, 8)); for fp16 it is below 0.002 in the tested range.
+  O      max over elements of (|O_gpu - O_ref| - half_ulp(O_gpu)) <= 1e-2. Subtracting half an
+         ulp removes the one unavoidable error -- rounding the exact result to the 16-bit
+         storage type -- which alone reaches 0.0078 (bf16, |O| in [2, 4)) and 0.0156 (|O| in
+         [4, 8)); for fp16 it is below 0.002 in the tested range. Where that rounding stays
+         small (bf16 |O| < 1, all of fp16) the raw max |O_gpu - O_ref| <= 1e-2 is asserted too.
   LSE    max |LSE_gpu - LSE_ref| <= 1e-3 (natural log units).
   dQ, dK, dV   ||X_gpu - X_ref||_F / ||X_ref||_F <= 2e-2, each tensor separately.
   delta  max_i |D_gpu,i - D_ref,i| / (||dO_i|| ||O_i|| + 1e-30) <= 1e-2. D is computed from the
@@ -67,8 +68,12 @@ def head_metrics(gpu, bits, dtype, b, h, scale, causal):
     ref = ORACLE.backward(q, k, v, do, scale, causal)
     o_gpu = gpu["o"][b, h]
     err_o = np.abs(o_gpu - ref["o"])
+    # the raw error where storage rounding alone stays well inside the gate: bf16 |O| < 1
+    # (half an ulp <= 2^-9), every fp16 value in the tested range (half an ulp < 0.002)
+    small = np.abs(o_gpu) < 1.0 if dtype == FI.BF16 else np.ones(o_gpu.shape, bool)
     m = {
         "o_raw": float(err_o.max()),
+        "o_raw_small": float(err_o[small].max()) if small.any() else 0.0,
         "o_gate": float((err_o - _lib.half_ulp(o_gpu, dtype)).max()),
         "lse": float(np.abs(gpu["lse"][b, h] - ref["lse"]).max()),
     }
@@ -82,6 +87,7 @@ def head_metrics(gpu, bits, dtype, b, h, scale, causal):
 def check(m, label):
     print(f"{label}: " + " ".join(f"{k}={v:.3g}" for k, v in m.items()), flush=True)
     assert m["o_gate"] <= TOL_O, (label, m)
+    assert m["o_raw_small"] <= TOL_O, (label, m)
     assert m["lse"] <= TOL_LSE, (label, m)
     for g in ("dq", "dk", "dv"):
         assert m[g] <= TOL_GRAD, (label, g, m)
