@@ -65,6 +65,9 @@ int main(void) {
   CHECK(fa_forward(q, k, v, o, lse, 1, 1, 16, 64, 2, 0.125f, FA_FP16, NULL) == FA_ERR_INVALID_ARG);
   CHECK(fa_forward(q, k, v, o, lse, 1, 1, 16, 64, 0, 0.125f, 7, NULL) == FA_ERR_INVALID_ARG);
   CHECK(fa_forward(q, k, v, q, lse, 1, 1, 16, 64, 0, 0.125f, FA_FP16, NULL) == FA_ERR_INVALID_ARG);
+  CHECK(fa_forward_pingpong(NULL, k, v, o, lse, 1, 1, 16, 128, 0, 0.125f, FA_BF16, NULL) == FA_ERR_INVALID_ARG);
+  CHECK(fa_forward_pingpong(q, k, v, q, lse, 1, 1, 16, 128, 1, 0.125f, FA_BF16, NULL) == FA_ERR_INVALID_ARG);
+  CHECK(fa_forward_pingpong(q, k, v, o, lse, 1, 1, 16, 132, 0, 0.125f, FA_BF16, NULL) == FA_ERR_UNSUPPORTED);
   CHECK(fa_forward(q, k, v, o, lse, 1, 1, 16, 100, 0, 0.125f, FA_FP16, NULL) == FA_ERR_UNSUPPORTED);
   CHECK(fa_forward(q, k, v, o, lse, 1, 1, 16, 264, 0, 0.125f, FA_BF16, NULL) == FA_ERR_UNSUPPORTED);
   CHECK(fa_backward(q, k, v, o, dO, lse, dq, dk, dv, NULL, 1, 1, 16, 64, 1, 0.125f, FA_BF16, NULL) ==
