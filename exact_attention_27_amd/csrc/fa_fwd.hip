@@ -84,8 +84,8 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
   // (n_qtiles-1-p, p), the heavy one first, so every workgroup has the same number of K/V tiles
   // (no tail of long-running workgroups at the end of the grid); an odd middle tile runs alone.
   // On a grid too small to fill the CUs twice over, one tile per workgroup, the heaviest first:
-  // the longest workgroup is then one heavy tile instead of a heavy and a light one. A head's workgroups run together on one
-  // XCD (shared K/V reads in its L2).
+  // the longest workgroup is then one heavy tile instead of a heavy and a light one. A head's
+  // workgroups run together on one XCD (shared K/V reads in its L2).
   // Split-KV: one workgroup per (head, Q tile, key range), no pairing.
   // The grid covers the longest sequence; a workgroup past its own sequence's tiles exits.
   const int BH = geo.B * geo.H;
@@ -548,17 +548,12 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
       __builtin_amdgcn_s_waitcnt(0x0F70 | CPWP);  // vmcnt(CPWP): the previous half-step's copies landed
       ring_barrier();
     };
-    // copies of K(tk) into slot (tk - t0) & 1, or of V(tv) into slot (tv - t0) & 1, spread by the halves
+    // copy c of this wave's share of K(tk) into slot (tk - t0) & 1
     auto copy_k = [&](int tk, int c) __attribute__((always_inline)) {
       const int tt = min(tk, last);
       const TileSrc r = tile_src<D, BN>(Kh, tt * BN, NK, rsk, dh);
       if (((tk - t0) & 1) == 0) stage_copy<D, BN, NW>(lds_k0, r, wave, c);
       else stage_copy<D, BN, NW>(lds_k1, r, wave, c);
-    };
-    auto copy_v = [&](int tv, int c) __attribute__((always_inline)) {
-      const TileSrc r = tile_src<D, BN>(Vh, tv * BN, NK, rsv, dh);
-      if (((tv - t0) & 1) == 0) stage_copy<D, BN, NW>(lds_v0, r, wave, c);
-      else stage_copy<D, BN, NW>(lds_v1, r, wave, c);
     };
     if (grpY) {
       // Y's idle first half-step: its share of K(t0 + 2)
