@@ -51,9 +51,10 @@ def both(fa, bits, dtype, causal, scale):
 
 # (B, H, N, d): one partial tile, ragged tails around the 256-row tile, several tiles, the
 # 128-wide kernel at d = 96, the default schedule at d = 64 and 256, a grid that pairs causal
-# tiles (B*H*8 pairs >= 2 per CU) and one that does not
+# tiles (B*H*8 pairs >= 2 per CU), one that pairs them with an odd middle tile running alone
+# (three 256-row tiles per head), and one that does not pair
 SHAPES = [(1, 2, 1, 128), (1, 2, 37, 128), (2, 3, 255, 128), (1, 2, 257, 128), (1, 3, 1000, 96),
-          (1, 2, 700, 64), (1, 2, 300, 256), (2, 8, 2048, 128), (4, 32, 4096, 128)]
+          (1, 2, 700, 64), (1, 2, 300, 256), (2, 8, 2048, 128), (4, 32, 4096, 128), (1, 512, 600, 128)]
 CASES = [(s, dt, c) for s in SHAPES for dt in (FI.BF16, FI.FP16) for c in (False, True)
          if not (s[0] * s[1] * s[2] >= 4 * 32 * 4096 and dt == FI.FP16)]
 
