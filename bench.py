@@ -2,7 +2,7 @@
 """Benchmark of the exact tiled attention path on one MI355X.
 
 One step = one full pass of the hot path over one batch of synthetic input resident in HBM:
-fa_forward (O, LSE) followed by the backward (preprocess delta, dK/dV, dQ -- the three
+fa_forward (O, LSE) followed by the backward (dQ computing delta, then dK/dV -- the two
 stages fa_backward runs, launched individually here so each kernel can be timed with HIP
 events on the stream it runs on).
 
@@ -15,8 +15,8 @@ Prints ONE JSON line on stdout. Progress goes to stderr.
 
 Besides the headline steps, the line carries "configs": every workload (and mask setting),
 each kernel timed as 11 runs on one stream, each bracketed by its own HIP events, enqueued
-back to back, the first discarded: the forward, the three backward stages one by one and one fa_backward call, with
-counted TFLOP/s (GB/s for the preprocess), the fraction of the chip's peak, the clock and
+back to back, the first discarded: the forward, its ping-pong form, the two backward stages
+one by one and one fa_backward call, with counted TFLOP/s, the fraction of the chip's peak, the clock and
 matrix-core utilisation each kernel ran at (from committed counter runs, when they match the
 current sources) and the fp64 oracle's forward and backward wall times on a sample of heads.
 
@@ -25,8 +25,8 @@ Options beyond the contract (--gpus, --steps, --warmup):
   --sweep                    also time the split-KV forward (2 and 4 ranges) on every workload,
                              and the strided, packed, other head-dim and decode (one query
                              against a key cache) problems
-  --counter-pass             no timing: launch every workload's four kernels 3 times each in a
-                             fixed order, for a rocprofv3 --pmc run that --ingest-sq reads
+  --counter-pass             no timing: launch every workload's kernels (STAGES) 3 times each in
+                             a fixed order, for a rocprofv3 --pmc run that --ingest-sq reads
   --ingest-sq SQ [FETCH WRITE]
                              no GPU work: turn the counter_collection.csv files of --counter-pass
                              rocprofv3 runs (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES,
@@ -55,17 +55,16 @@ N_XCDS = 8                  # GRBM_GUI_ACTIVE sums the 8 XCDs' cycle counts
 COUNTER_REPEATS = 3         # launches of each kernel per workload in a --counter-pass run
 # the kernels of a step, plus the forward's two-group ping-pong form (fa_forward_pingpong),
 # timed and counted beside them on every workload
-STAGES = ("fwd", "fwd_pingpong", "bwd_preprocess", "bwd_dkv", "bwd_dq")
+STAGES = ("fwd", "fwd_pingpong", "bwd_dq_delta", "bwd_dkv")
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
     "fwd_pingpong": ["fa_fwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
-    "bwd_preprocess": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
     "bwd_dkv": ["fa_bwd_dkv.hip", "fa_common.hpp", "fa_kernels.hpp"],
-    "bwd_dq": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
+    "bwd_dq_delta": ["fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp"],
 }
 # Kernel-name fragments of each timed kernel in a profiler's per-dispatch records.
-KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "fwd_pingpong": "fwd_kernel", "bwd_preprocess": "bwd_preprocess_kernel",
-                  "bwd_dkv": "bwd_dkv_kernel", "bwd_dq": "bwd_dq_kernel"}
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "fwd_pingpong": "fwd_kernel", "bwd_dkv": "bwd_dkv_kernel",
+                  "bwd_dq_delta": "bwd_dq_kernel"}
 
 
 def log(*a):
@@ -86,9 +85,8 @@ def algorithmic_bytes(kernel: str, w) -> float:
     t, r = w.B * w.H * w.N * w.d * 2, w.B * w.H * w.N * 4
     return {"fwd": 4 * t + r,                   # Q, K, V in; O, LSE out
             "fwd_pingpong": 4 * t + r,
-            "bwd_preprocess": 2 * t + r,        # O, dO in; delta out
             "bwd_dkv": 6 * t + 2 * r,           # Q, K, V, dO, LSE, delta in; dK, dV out
-            "bwd_dq": 5 * t + 2 * r}[kernel]    # Q, K, V, dO, LSE, delta in; dQ out
+            "bwd_dq_delta": 6 * t + 2 * r}[kernel]  # Q, K, V, O, dO, LSE in; dQ, delta out
 
 
 def traffic_for(kernel: str, workload: str, causal: bool = True):
@@ -332,32 +330,30 @@ def _config_tensors(FI, torch, np, dev, w):
 
 
 def _stage_fns(fa, t, causal, scale, stream):
-    """The four kernels of a step and the ping-pong forward, each as one call."""
+    """The kernels of a step (forward; dQ with delta; dK/dV) and the ping-pong forward, each as
+    one call, in an order that lets each consume what the previous ones wrote."""
     return {
         "fwd": lambda: fa.fa_forward(t["q"], t["k"], t["v"], t["o"], t["lse"], causal, scale, stream),
         "fwd_pingpong": lambda: fa.fa_forward_pingpong(t["q"], t["k"], t["v"], t["o"], t["lse"], causal, scale,
                                                        stream),
-        "bwd_preprocess": lambda: fa.fa_backward_preprocess(t["o"], t["do"], t["delta"], stream),
         "bwd_dkv": lambda: fa.fa_backward_dkv(t["q"], t["k"], t["v"], t["do"], t["lse"], t["delta"], t["dk"], t["dv"],
                                               causal, scale, stream),
-        "bwd_dq": lambda: fa.fa_backward_dq(t["q"], t["k"], t["v"], t["do"], t["lse"], t["delta"], t["dq"], causal,
-                                            scale, stream),
+        "bwd_dq_delta": lambda: fa.fa_backward_dq_delta(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["dq"],
+                                                        t["delta"], causal, scale, stream),
     }
 
 
 def kernel_work(name, w, causal):
     """Algorithmic work of one launch of a kernel on workload w: (bound, amount, unit, peak).
     Forward F = 4 B H N^2 d, halved for causal; dK/dV 2F (S, dP, dV, dK); dQ 0.5F (dQ only: its
-    S and dP recomputation is the price of having no atomics and is not counted); the
-    preprocess reads O and dO and writes delta (bytes)."""
+    S and dP recomputation is the price of having no atomics, and its D computation, are not
+    counted)."""
     F = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if causal else 1.0)
-    rows = w.B * w.H * w.N
     return {
         "fwd": ("mfma", F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
         "fwd_pingpong": ("mfma", F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
         "bwd_dkv": ("mfma", 2.0 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-        "bwd_dq": ("mfma", 0.5 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-        "bwd_preprocess": ("hbm", (2 * rows * w.d * 2 + rows * 4) / 1e9, "GB/s", PEAK_HBM_GBS),
+        "bwd_dq_delta": ("mfma", 0.5 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
     }[name]
 
 
@@ -549,7 +545,7 @@ def ingest_sq(csv_path: str, write: bool = True) -> dict:
         bound, work, unit, _ = kernel_work(st, w, causal)
         if bound == "mfma" and "SQ_INSTS_MFMA" in ds[0]:
             # products the kernel's algorithm needs: the counted work, and for dQ its S and dP too
-            executed = {"fwd": 1.0, "fwd_pingpong": 1.0, "bwd_dkv": 1.0, "bwd_dq": 3.0}[st]
+            executed = {"fwd": 1.0, "fwd_pingpong": 1.0, "bwd_dkv": 1.0, "bwd_dq_delta": 3.0}[st]
             rec["mfma_issued_per_needed"] = (sum(d["SQ_INSTS_MFMA"] for d in ds) / len(ds)) / (work * 1e12 * executed / 32768)
         out[f"{key}|{int(causal)}|{st}"] = rec
     if write:
@@ -636,7 +632,7 @@ def main():
     log(f"inputs drawn and resident in HBM in {time.perf_counter() - t0:.1f} s")
 
     stream = torch.cuda.current_stream(dev)
-    names = ["fwd", "bwd_preprocess", "bwd_dkv", "bwd_dq"]
+    names = ["fwd", "bwd_dq_delta", "bwd_dkv"]
 
     def step(evs=None):
         if evs:
@@ -644,21 +640,18 @@ def main():
         fa.fa_forward(q, k, v, o, lse, causal, scale, stream)
         if evs:
             evs[1].record(stream)
-        fa.fa_backward_preprocess(o, do, delta, stream)
+        fa.fa_backward_dq_delta(q, k, v, o, do, lse, dq, delta, causal, scale, stream)
         if evs:
             evs[2].record(stream)
         fa.fa_backward_dkv(q, k, v, do, lse, delta, dk, dv, causal, scale, stream)
         if evs:
             evs[3].record(stream)
-        fa.fa_backward_dq(q, k, v, do, lse, delta, dq, causal, scale, stream)
-        if evs:
-            evs[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -676,19 +669,13 @@ def main():
     step_flops = 3.5 * F
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = F / (kern_ms["fwd"] * 1e-3) / 1e12
-    bwd_ms = kern_ms["bwd_preprocess"] + kern_ms["bwd_dkv"] + kern_ms["bwd_dq"]
+    bwd_ms = kern_ms["bwd_dq_delta"] + kern_ms["bwd_dkv"]
     bwd_tflops = 2.5 * F / (bwd_ms * 1e-3) / 1e12
 
-    # Algorithmic work per launch: forward F; dK/dV kernel 2F (S, dP,
-    # dV, dK); dQ kernel 0.5F (dQ only -- its S and dP recomputation is the price of having
-    # no atomics and is not counted); preprocess reads O and dO and writes delta (bytes).
-    rows = w.B * w.H * w.N
-    algo = {
-        "fwd": ("mfma", F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-        "bwd_dkv": ("mfma", 2.0 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-        "bwd_dq": ("mfma", 0.5 * F / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-        "bwd_preprocess": ("hbm", (2 * rows * w.d * 2 + rows * 4) / 1e9, "GB/s", PEAK_HBM_GBS),
-    }
+    # Algorithmic work per launch (kernel_work): forward F; dK/dV kernel 2F (S, dP, dV, dK);
+    # dQ kernel 0.5F (dQ only -- its S and dP recomputation is the price of having no atomics,
+    # and its D computation, are not counted).
+    algo = {n: kernel_work(n, w, causal) for n in names}
     dominant = max(kern_ms, key=kern_ms.get)
     bound, work, unit, peak = algo[dominant]
     achieved = work / (kern_ms[dominant] * 1e-3)

@@ -31,7 +31,7 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
 EXPORTED_SYMBOLS = ("fa_forward", "fa_forward_pingpong", "fa_forward_splitkv", "fa_forward_splitkv_workspace_bytes", "fa_backward",
-                    "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_forward_ex", "fa_backward_ex",
+                    "fa_backward_preprocess", "fa_backward_dkv", "fa_backward_dq", "fa_backward_dq_delta", "fa_forward_ex", "fa_backward_ex",
                     "fa_forward_splitkv_ex", "fa_forward_splitkv_ex_workspace_bytes", "fa_backward_noalloc",
                     "fa_backward_noalloc_max_rows", "fa_status_string")
 
@@ -83,6 +83,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dkv.restype = i
     lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_backward_dq.restype = i
+    lib.fa_backward_dq_delta.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_backward_dq_delta.restype = i
     S, P = FAStrides, ctypes.POINTER(FAProblem)
     lib.fa_forward_ex.argtypes = [P, vp, S, vp, S, vp, S, vp, S, vp, vp]
     lib.fa_forward_ex.restype = i
@@ -301,6 +303,17 @@ def fa_backward_dq(q, k, v, do, lse, delta, dq, causal: bool, scale: float, stre
                  B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream, q.device))
     if st != FA_OK:
         raise FAError(st, "fa_backward_dq")
+
+
+def fa_backward_dq_delta(q, k, v, o, do, lse, dq, delta, causal: bool, scale: float, stream=None) -> None:
+    """Backward stages 1 and 3 in one launch: dQ, with D computed from o and dO and written to delta."""
+    B, H, N, d = _check_stage(q, k, v, do, lse, delta, (("dq", dq), ("o", o)))
+    _one_device(q.device, k=k, v=v, o=o, do=do, lse=lse, delta=delta, dq=dq)
+    st = _invoke("fa_backward_dq_delta", q.device, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                 _ptr(dq), _ptr(delta), B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
+                 _stream_handle(stream, q.device))
+    if st != FA_OK:
+        raise FAError(st, "fa_backward_dq_delta")
 
 
 def attention_forward(q, k, v, causal: bool, scale: float | None = None, stream=None):

@@ -448,9 +448,13 @@ int fa_backward_ex(const fa_problem* p, const void* q, fa_strides sq, const void
   if (st != FA_OK) return st;
   if (nothing_to_do_bwd(*p)) return FA_OK;
   a.stream = stream;
-  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_dkv(a) != hipSuccess) return FA_ERR_HIP;
+  // dQ first: each of its workgroups also computes D for its own query rows and writes delta,
+  // which the dK/dV stage then reads (the preprocess stage's work, without its extra pass
+  // over dO)
+  a.dq_delta = true;
   if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_HIP;
+  a.dq_delta = false;
+  if (fa::launch_bwd_dkv(a) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 
@@ -498,6 +502,21 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, 
                      false, true, false, &a);
   if (st != FA_OK) return st;
   a.stream = stream;
+  return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                         const float* lse, void* dq, float* delta, int B, int H, int N, int d, int causal,
+                         float scale, int dtype, void* stream) {
+  fa::BwdArgs a;
+  const fa_problem p = fixed_problem(B, H, N, d, causal, scale, dtype);
+  const fa_strides c = contiguous(H, N, d);
+  // delta is an output here
+  int st = check_bwd(&p, q, c, k, c, v, c, o, c, dO, c, lse, dq, c, nullptr, c, nullptr, c, delta, true, true, true,
+                     false, &a);
+  if (st != FA_OK) return st;
+  a.stream = stream;
+  a.dq_delta = true;
   return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -83,7 +83,8 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, Geom geo, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdq,
-    int n_qtiles_max, int pair, float scale, float c_log2) {
+    int n_qtiles_max, int pair, float scale, float c_log2, const uint16_t* __restrict__ O, Strides so,
+    float* __restrict__ DeltaOut) {
   constexpr int KB = BN / 32;  // 32-key blocks per K/V tile
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;
@@ -161,7 +162,28 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dq_kernel(
       dof[ks].v = gload16(dOh + (size_t)qrow * rsdo + ks * 16 + h * 8, okc);
     }
     lse2 = ok ? LSE[sq_.stat + qrow] * kLog2e : 0.f;
-    dl = ok ? Delta[sq_.stat + qrow] : 0.f;
+    if (O != nullptr) {
+      // With O given, this workgroup computes D for its own rows in place of the preprocess
+      // stage, by the same definition (D_i = sum_c dO_ic O_ic from the stored O, fp32): the
+      // lane's half of the row (the columns of its dO fragments), then its partner lane's half,
+      // and writes it for the dK/dV stage.
+      const uint16_t* Oh = seq_base(O, so, sq_);
+      float part = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ov = gload16(Oh + (size_t)qrow * so.r + ks * 16 + h * 8, ok && ks * 16 + h * 8 < dh);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t g = dof[ks].v[w];
+          part = __builtin_fmaf(T::to_f32((uint16_t)(ov[w] & 0xffff)), T::to_f32((uint16_t)(g & 0xffff)), part);
+          part = __builtin_fmaf(T::to_f32((uint16_t)(ov[w] >> 16)), T::to_f32((uint16_t)(g >> 16)), part);
+        }
+      }
+      dl = half_swap_sum(part);
+      if (ok && h == 0) DeltaOut[sq_.stat + qrow] = dl;
+    } else {
+      dl = ok ? Delta[sq_.stat + qrow] : 0.f;
+    }
   }
 
   f32x16 acc[DB];
@@ -357,7 +379,8 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   return launch_kernel(&bwd_dq_kernel<T, D, BN, NW, CAUSAL>, (unsigned)grid, NW * 64, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.delta,
                        (uint16_t*)a.dq, a.g, a.sq, a.sk, a.sv, a.sdo, a.sdq, n_qtiles, pair ? 1 : 0, a.scale,
-                       a.c_log2);
+                       a.c_log2, a.dq_delta ? (const uint16_t*)a.o : nullptr, a.so,
+                       a.dq_delta ? a.delta : nullptr);
 }
 
 template <typename T>

@@ -72,6 +72,7 @@ struct BwdArgs {
   float scale;
   float c_log2;
   void* stream;
+  bool dq_delta = false;  // the dQ stage computes D from o and dO and writes it to delta
 };
 
 // Launch `kern` and return the status of this launch alone. hipLaunchKernel reports the

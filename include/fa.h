@@ -11,11 +11,11 @@
  *             the result is the standard attention result, not an approximation
  *             ("FlashAttentionを1から", section "オンラインsoftmax").
  *   backward  dQ, dK, dV for an upstream gradient dO, recomputing P = exp(S - LSE)
- *             from the saved LSE and using D_i = rowsum(dO_i * O_i), in three kernels
- *             (preprocess D; dK/dV with a pinned K/V tile; dQ with a pinned Q tile)
- *             so that every output tile has exactly one writer and no atomics are used
- *             ("Triton 05: Flash Attention", sections "Softmax Gradient" and
- *             "3단계 커널 구조").
+ *             from the saved LSE and using D_i = rowsum(dO_i * O_i), in three stages
+ *             (D; dK/dV with a pinned K/V tile; dQ with a pinned Q tile) so that every
+ *             output tile has exactly one writer and no atomics are used ("Triton 05:
+ *             Flash Attention", sections "Softmax Gradient" and "3단계 커널 구조");
+ *             fa_backward runs the D stage inside the dQ kernel, in two launches.
  *
  * Conventions shared by every entry point:
  *
@@ -147,7 +147,8 @@ size_t fa_forward_splitkv_workspace_bytes(int B, int H, int N, int d, int num_sp
  *   delta    out: (B, H, N) float32 caller-provided workspace; on return (in stream
  *                 order) it holds D_i = sum_c dO_ic * O_ic, computed from the stored
  *                 O. Must not be NULL.
- * Three kernel launches on `stream`, in order: preprocess (delta), dK/dV, dQ.
+ * Two kernel launches on `stream`, in order: dQ, whose workgroups also compute D for their
+ * own query rows and write delta (fa_backward_dq_delta), then dK/dV (fa_backward_dkv).
  * Returns an fa_status.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
@@ -156,15 +157,20 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 int dtype, void* stream);
 
 /*
- * The three backward stages, individually. fa_backward() is exactly these three calls in
- * this order on one stream; they are exported so a caller can interleave its own work or
- * time each kernel. Arguments have the same meaning, rules and errors as in fa_backward().
- *   fa_backward_preprocess  delta_i = sum_c dO_ic * O_ic            ("Triton 05", "3단계 커널
- *                           구조", stage 1). Reads o, dO; writes delta.
+ * The backward stages, individually, for callers that interleave their own work or time each
+ * kernel. Arguments have the same meaning, rules and errors as in fa_backward(). The pages
+ * split the backward into three kernels ("Triton 05", "3단계 커널 구조"); fa_backward() runs
+ * the first inside the third, as fa_backward_dq_delta then fa_backward_dkv on one stream.
+ *   fa_backward_preprocess  delta_i = sum_c dO_ic * O_ic (stage 1). Reads o, dO; writes delta.
  *   fa_backward_dkv         dK, dV with one K/V tile pinned per workgroup, looping over Q
  *                           tiles (stage 2). Reads q, k, v, dO, lse, delta; writes dk, dv.
  *   fa_backward_dq          dQ with one Q tile pinned per workgroup, looping over K/V tiles
  *                           (stage 3). Reads q, k, v, dO, lse, delta; writes dq.
+ *   fa_backward_dq_delta    stages 1 and 3 in one launch: each dQ workgroup computes D for its
+ *                           own query rows from o and dO (the definition of stage 1, fp32),
+ *                           writes it to delta and uses it. Reads q, k, v, o, dO, lse; writes
+ *                           dq, delta. Its D (and so dq) may differ from the two-launch form by
+ *                           fp32 summation order.
  */
 int fa_backward_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
                            int dtype, void* stream);
@@ -174,6 +180,9 @@ int fa_backward_dkv(const void* q, const void* k, const void* v, const void* dO,
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                    const float* delta, void* dq, int B, int H, int N, int d, int causal, float scale,
                    int dtype, void* stream);
+int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, void* dq, float* delta, int B, int H,
+                         int N, int d, int causal, float scale, int dtype, void* stream);
 
 /*
  * Strided operands and variable-length batches.
@@ -236,7 +245,7 @@ typedef struct {
 int fa_forward_ex(const fa_problem* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
                   const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* stream);
 
-/* fa_backward() on strided operands / variable-length batches (rules above): the same three
+/* fa_backward() on strided operands / variable-length batches (rules above): the same two
  * kernels in the same order on `stream`. */
 int fa_backward_ex(const fa_problem* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
                    const void* v, fa_strides sv, const void* o, fa_strides so, const void* dO,

@@ -10,9 +10,8 @@ import fa_inputs as FI
 
 NAMES = {"fwd": "void fa::fwd_kernel<fa::BF16, 128, 64, 4, true, false>(int)",
          "fwd_pingpong": "void fa::fwd_kernel<fa::BF16, 128, 64, 8, true, false>(int)",
-         "bwd_preprocess": "void fa::bwd_preprocess_kernel<fa::BF16, 128>(int)",
          "bwd_dkv": "void fa::bwd_dkv_kernel<fa::BF16, 128, 4, true>(int)",
-         "bwd_dq": "void fa::bwd_dq_kernel<fa::BF16, 128, 64, 4, true>(int)"}
+         "bwd_dq_delta": "void fa::bwd_dq_kernel<fa::BF16, 128, 64, 4, true>(int)"}
 
 
 def _write_csv(path, order, ns=1_000_000, gui=None, busy=None, extra_first=True, counters=None, copy=None):
@@ -81,9 +80,9 @@ def test_kernel_work_counts():
     F = 4.0 * 4 * 32 * 4096 * 4096 * 128 * 0.5
     assert bench.kernel_work("fwd", w, True)[1] == pytest.approx(F / 1e12)
     assert bench.kernel_work("bwd_dkv", w, True)[1] == pytest.approx(2 * F / 1e12)
-    assert bench.kernel_work("bwd_dq", w, True)[1] == pytest.approx(0.5 * F / 1e12)
-    rows = 4 * 32 * 4096
-    assert bench.kernel_work("bwd_preprocess", w, True)[1] == pytest.approx((2 * rows * 128 * 2 + rows * 4) / 1e9)
+    assert bench.kernel_work("bwd_dq_delta", w, True)[1] == pytest.approx(0.5 * F / 1e12)
+    t, rows = 4 * 32 * 4096 * 128 * 2, 4 * 32 * 4096 * 4
+    assert bench.algorithmic_bytes("bwd_dq_delta", w) == 6 * t + 2 * rows
 
 
 def test_ingest_traffic_scales_by_the_copy(tmp_path, monkeypatch):
@@ -93,7 +92,7 @@ def test_ingest_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "c.json"))
     sq, fe, wr = tmp_path / "sq.csv", tmp_path / "f.csv", tmp_path / "w.csv"
     _write_csv(sq, _plan())
-    kib = {"fwd": 1000.0, "fwd_pingpong": 1100.0, "bwd_preprocess": 2000.0, "bwd_dkv": 3000.0, "bwd_dq": 4000.0}
+    kib = {"fwd": 1000.0, "fwd_pingpong": 1100.0, "bwd_dkv": 3000.0, "bwd_dq_delta": 4000.0}
     _write_csv(fe, _plan(), counters=lambda st: (("FETCH_SIZE", kib[st]),), copy=("FETCH_SIZE", 64 * 1024.0))
     _write_csv(wr, _plan(), counters=lambda st: (("WRITE_SIZE", kib[st] / 2),), copy=("WRITE_SIZE", 256 * 1024.0))
     table = bench.ingest_traffic(str(fe), str(wr), 256, bench.ingest_sq(str(sq), write=False))

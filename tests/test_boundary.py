@@ -111,6 +111,13 @@ def test_stage_validation(lib):
     assert lib.fa_backward_dq(*args[:6], args[5], 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_backward_dq(*args[:6], vp(0), 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_backward_dq(*args[:7], 1, 1, 16, 64, 0, -0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    # dq with delta: q k v o dO lse dq delta (o is read, delta written)
+    dd = [vp(x) for x in A[:8]]
+    assert lib.fa_backward_dq_delta(*dd[:3], vp(0), *dd[4:], 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dq_delta(*dd[:7], vp(0), 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dq_delta(*dd[:7], dd[3], 1, 1, 16, 64, 0, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dq_delta(*dd, 1, 1, 16, 64, 2, 0.1, 0, vp(0)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_dq_delta(*dd, 1, 1, 16, 60, 0, 0.1, 0, vp(0)) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors(lib):
