@@ -79,6 +79,10 @@ int main(void) {
         FA_ERR_INVALID_ARG);
   CHECK(fa_backward_dq(q, k, v, dO, lse, delta, NULL, 1, 1, 16, 64, 1, 0.125f, FA_BF16, NULL) ==
         FA_ERR_INVALID_ARG);
+  CHECK(fa_backward_dq_delta(q, k, v, NULL, dO, lse, dq, delta, 1, 1, 16, 64, 1, 0.125f, FA_BF16, NULL) ==
+        FA_ERR_INVALID_ARG);
+  CHECK(fa_backward_dq_delta(q, k, v, o, dO, lse, dq, delta, 1, 1, 16, 72 + 1, 1, 0.125f, FA_BF16, NULL) ==
+        FA_ERR_UNSUPPORTED);
   CHECK(fa_forward_splitkv(q, k, v, o, lse, 1, 1, 16, 64, 0, 0.125f, FA_FP16, 0, (float*)addr(10), 1 << 20,
                            NULL) == FA_ERR_INVALID_ARG); /* zero splits */
 
