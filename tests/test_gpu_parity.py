@@ -285,3 +285,55 @@ def test_very_long_sequence_sampled_rows(fa):
     dv_gap = float((dv32.sum(0) - do32.sum(0)).abs().max() / dv32.abs().sum(0).max())
     print(f"N=2^20 invariants: |sum dK|/sum|dK|={dk_sum:.3g} |sum dV - sum dO|/sum|dV|={dv_gap:.3g}", flush=True)
     assert dk_sum <= 1e-2 and dv_gap <= 1e-2
+
+
+def test_tensors_past_2_31_elements(fa):
+    """B=64 H=32 N=8192 d=128 (causal, bf16): every (B, H, N, d) tensor holds 2^31 elements
+    (4 GiB), so the last heads sit past any 32-bit element offset. Inputs are N(0,1) draws of
+    torch's seeded generator on the device, rounded to bf16; the oracle gets the same bits of
+    the sampled heads. For the first and the last head: sampled rows of O, LSE and dQ against
+    the oracle's row-restricted definitions, and dK, dV through sum_j dK_j = 0 and
+    sum_j dV_j = sum_i dO_i; every output finite."""
+    import torch
+    B, H, N, d, dtype, causal = 64, 32, 8192, 128, FI.BF16, True
+    scale = d ** -0.5
+    gen = torch.Generator(device="cuda").manual_seed(9400)
+    ins = []
+    for _ in range(4):
+        t = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+        for b in range(B):  # one batch at a time: a float32 draw of 2^31 values would take 8 GiB
+            t[b] = torch.randn((H, N, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        ins.append(t)
+    q, k, v, do = ins
+    o, dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(4))
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device)
+    delta = torch.full_like(lse, float("nan"))
+    fa.fa_forward(q, k, v, o, lse, causal, scale)
+    fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, delta, causal, scale)
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv, delta):
+        assert bool(torch.isfinite(t).all())
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N),
+                                     np.random.Generator(np.random.PCG64(9401)).integers(8, N - 8, 16)]))
+    idx = torch.from_numpy(rows).to(q.device)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        bits = {n: t[b, h].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                for n, t in zip(FI.TENSOR_ORDER, ins)}
+        qf, kf, vf, dof = (FI.bits_to_f64(bits[n], dtype) for n in FI.TENSOR_ORDER)
+        o_np = _lib.from_device(o[b, h].index_select(0, idx), dtype)
+        dq_np = _lib.from_device(dq[b, h].index_select(0, idx), dtype)
+        lse_np = lse[b, h].index_select(0, idx).cpu().numpy().astype(np.float64)
+        o_ref, lse_ref = ORACLE.forward_rows(qf, kf, vf, scale, causal, rows)
+        dq_ref = ORACLE.dq_rows(qf, kf, vf, dof, scale, causal, rows)
+        gate = float((np.abs(o_np - o_ref) - _lib.half_ulp(o_np, dtype)).max())
+        lerr = float(np.abs(lse_np - lse_ref).max())
+        dq_rel = float(np.linalg.norm(dq_np - dq_ref) / np.linalg.norm(dq_ref))
+        dk64, dv64, do64 = dk[b, h].double(), dv[b, h].double(), do[b, h].double()
+        dk_sum = float(dk64.sum(0).abs().max() / dk64.abs().sum(0).max())
+        dv_gap = float((dv64.sum(0) - do64.sum(0)).abs().max() / dv64.abs().sum(0).max())
+        print(f"b{b}h{h}: o_gate={gate:.3g} lse={lerr:.3g} dq_rel={dq_rel:.3g} "
+              f"|sum dK|/sum|dK|={dk_sum:.3g} |sum dV - sum dO|/sum|dV|={dv_gap:.3g}", flush=True)
+        assert gate <= TOL_O and lerr <= TOL_LSE and dq_rel <= TOL_GRAD
+        assert dk_sum <= 1e-2 and dv_gap <= 1e-2
+    del q, k, v, do, o, dq, dk, dv, ins
+    torch.cuda.empty_cache()
