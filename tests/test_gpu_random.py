@@ -20,7 +20,7 @@ from tests.test_gpu_rectangular import compare_head
 
 pytestmark = pytest.mark.gpu
 
-N_DRAWS = 120
+N_DRAWS = 520
 
 
 @pytest.fixture(scope="module")

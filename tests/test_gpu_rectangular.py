@@ -57,7 +57,17 @@ def compare_head(got, ref, dtype, label, grads=True):
         for g in ("dq", "dk", "dv"):
             nrm = np.linalg.norm(ref[g])
             if nrm == 0.0:
-                assert np.all(got[g] == 0.0), f"{label}: {g} should be zero"
+                if g == "dv":
+                    # dV_j = sum_i P_ij dO_i: zero only when no query sees the key, which the
+                    # kernel writes as exact zeros
+                    assert np.all(got[g] == 0.0), f"{label}: {g} should be zero"
+                else:
+                    # A sequence with one visible key has dS = P (dP - D) = 0 exactly, but the
+                    # kernels take dP = dO.V from the matrix cores and D = dO.O from the stored
+                    # O (reading of the pages: D comes from the saved O), two fp32 sums of the
+                    # same products in different orders: dQ and dK are then rounding-sized,
+                    # as in the one-key case of the parity tests.
+                    assert np.abs(got[g]).max() <= 1e-3, f"{label}: {g} should be (rounding-)zero"
                 m[g] = 0.0
             else:
                 m[g] = float(np.linalg.norm(got[g] - ref[g]) / nrm)
