@@ -5,7 +5,9 @@ Each draw (numpy PCG64, seed 8000 + index, fixed before any result) picks:
     sequence (zero lengths included), with shared or separate key offsets;
   * a head dim (any multiple of 8 up to 256), fp16 or bf16, causal or not, and a scale;
   * the storage layout: (B,H,N,d), or (B,N,H,d) / packed rows with padding columns after d.
-It runs fa_forward_ex + fa_backward_ex, and for half of the draws also fa_forward_splitkv_ex.
+It runs fa_forward_ex + fa_backward_ex, and for half of the draws also fa_forward_splitkv_ex;
+for contiguous fixed-length draws with as many keys as queries, fa_forward_pingpong too (bit
+for bit against fa_forward_ex).
 Every head of every sequence is compared with the fp64 oracle to the tolerances of
 tests/test_gpu_parity.py. Rows that see no key must be exactly O = 0, LSE = -inf, dQ = 0. Keys
 that no query sees must get dK = dV = 0.
@@ -138,6 +140,14 @@ def test_random_problem(fa, i):
         fa.fa_forward_splitkv_ex(q, k, v, o2, lse2, causal, scale, p["split"], None, **kw)
         torch.cuda.synchronize()
         split = (to_np(o2), lse2.cpu().numpy().astype(np.float64))
+
+    if not p["varlen"] and p["layout"] == "bhnd" and p["pad"] == 0 and p["nq"] == p["nk"]:
+        # the ping-pong forward on the same contiguous problem: bit for bit what fa_forward_ex gave
+        o3 = torch.full_like(q, nan)
+        lse3 = torch.full_like(lse, nan)
+        fa.fa_forward_pingpong(q, k, v, o3, lse3, causal, scale)
+        torch.cuda.synchronize()
+        assert o3.equal(o) and lse3.equal(lse), f"draw {i}: ping-pong forward differs"
 
     for b, h, qi, ki, si in cases:
         qf, dof, kf, vf = qb[qi], dob[qi], kb[ki], vb[ki]
