@@ -291,7 +291,8 @@ int forward_impl(const fa_problem* pp, const void* q, const fa_strides& sq, cons
 }
 
 // Backward validation. Null pointers are operands a stage does not use (their strides are
-// ignored); `delta` is an output of the preprocess stage (need_o) and an input otherwise.
+// ignored); `delta` is an output of the stages that compute D from O (need_o: the preprocess
+// stage, dQ with D, the whole backward) and an input otherwise.
 int check_bwd(const fa_problem* pp, const void* q, const fa_strides& sq, const void* k, const fa_strides& sk,
               const void* v, const fa_strides& sv, const void* o, const fa_strides& so, const void* dO,
               const fa_strides& sdo, const float* lse, const void* dq, const fa_strides& sdq, const void* dk,

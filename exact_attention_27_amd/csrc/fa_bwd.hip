@@ -1,4 +1,4 @@
-// Exact tiled attention backward for gfx950: three kernels, no atomics.
+// Exact tiled attention backward for gfx950: three stages, no atomics.
 //
 // "Triton 05: Flash Attention", sections "Backward 구현", "LSE로 P 재계산", "Softmax Gradient"
 // and "3단계 커널 구조": P is rebuilt from the saved LSE (P_ij = exp(S_ij - LSE_i)), the
@@ -9,6 +9,9 @@
 //                    dV += P^T dO,  dP = dO V^T,  dS = P*(dP - D),  dK += scale * dS^T Q
 //   [3] dQ         : one workgroup per Q tile (pinned in VGPRs), loop over K/V tiles
 //                    dP = dO V^T,  dS = P*(dP - D),  dQ += scale * dS K
+// Stage [1] also runs inside [3]: given O, each dQ workgroup computes D for the query rows it
+// owns (it holds their dO already) and writes it, so the full backward is [3] then [2], two
+// launches, with no separate pass over O and dO.
 // All products run on the matrix cores with fp32 accumulation; P and dS are rounded to the
 // input type (nearest even) as matrix-core operands. Operands whose contraction index runs
 // down the rows of a staged tile (Q^T, dO^T, K^T) are read with the transposing LDS load.

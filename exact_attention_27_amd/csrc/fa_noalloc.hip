@@ -8,9 +8,9 @@
 // holds its own). Its address on a device comes from hipGetSymbolAddress, taken once per device
 // with that device current and cached; host code uses only that address (the array's name is a
 // host-side stand-in, not a device address). Every call on one GPU shares the array: calls
-// that overlap in time on one GPU (e.g. on two streams) race on it. The preprocess kernel
-// writes every D_i the other two kernels read before they read it, so nothing has to start
-// at zero and no clearing is needed between calls.
+// that overlap in time on one GPU (e.g. on two streams) race on it. The dQ kernel writes
+// every D_i that it and the dK/dV kernel read before they read it, so nothing has to start at
+// zero and no clearing is needed between calls.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
