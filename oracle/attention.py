@@ -131,11 +131,18 @@ def dq_rows(q, k, v, do, scale: float, causal: bool, rows):
     return scale * (ds @ k)
 
 
-def backward(q, k, v, do, scale: float, causal: bool):
+def backward(q, k, v, do, scale: float, causal: bool, o_stored=None):
     """Exact attention backward for one head.
 
     Returns a dict with o, lse, dq, dk, dv and delta (D_i = rowsum(dO_i * O_i)),
     all float64.
+
+    o_stored: None for the softmax Jacobian form above. Otherwise the output as a
+    kernel stored it (16-bit values, as float64): dS then uses D_i = rowsum(dO_i * O_i)
+    of that stored O, the preprocess step of "Triton 05", section "3단계 커널 구조",
+    evaluated exactly. With the exact O the two forms agree (sum_k P_ik dP_ik =
+    dO_i . (P V)_i); they differ by the rounding of the stored O, which dominates dS
+    where dS is a small difference (a row with two or three visible keys, say).
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -144,7 +151,10 @@ def backward(q, k, v, do, scale: float, causal: bool):
     o, lse, p = forward(q, k, v, scale, causal, return_p=True)
     dv = p.T @ do
     dp = do @ v.T
-    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    if o_stored is None:
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    else:
+        ds = p * (dp - (do * _as_f64(o_stored)).sum(axis=1, keepdims=True))
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     delta = (do * o).sum(axis=1)

@@ -162,7 +162,7 @@ def test_random_problem(fa, i):
         ref = ORACLE.backward(qf, kf, vf, dof, scale, causal)
         got = {"o": g["o"][qi], "lse": g_lse[si], "dq": g["dq"][qi], "dk": g["dk"][ki], "dv": g["dv"][ki],
                "delta": g_delta[si], "do_in": dof}
-        compare_head(got, ref, dtype, lab)
+        compare_head(got, ref, dtype, lab, inputs=(qf, kf, vf, dof, scale, causal))
         if split is not None:
             compare_head({"o": split[0][qi], "lse": split[1][si]}, {"o": ref["o"], "lse": ref["lse"]}, dtype,
                          f"{lab} split={p['split']}", grads=False)

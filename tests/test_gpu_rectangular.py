@@ -41,9 +41,15 @@ def _nan_like(t, shape=None):
     return torch.full(shape, float("nan"), dtype=torch.float32, device=t.device)
 
 
-def compare_head(got, ref, dtype, label, grads=True):
+def compare_head(got, ref, dtype, label, grads=True, inputs=None):
     """Oracle comparison of one head. got / ref: dicts of float64 arrays (o, lse[, dq, dk, dv,
-    delta]). Rows the oracle gives LSE = -inf must be exactly O = 0 / LSE = -inf / dQ = 0."""
+    delta]). Rows the oracle gives LSE = -inf must be exactly O = 0 / LSE = -inf / dQ = 0.
+
+    inputs (q, k, v, dO, scale, causal as float64): when dQ or dK misses the gate, the head is
+    also compared with the oracle's backward that takes D from the GPU's stored O (reading of
+    the pages: the preprocess step uses the saved O). It passes only if the rounding of that O
+    moves the reference by more than half the gate (dS is then a small difference of rounded
+    terms: a row with two or three visible keys, say) and the GPU meets the gate against it."""
     m = {}
     err = np.abs(got["o"] - ref["o"])
     m["o_gate"] = float((err - _lib.half_ulp(got["o"], dtype)).max()) if err.size else 0.0
@@ -76,8 +82,18 @@ def compare_head(got, ref, dtype, label, grads=True):
     print(f"{label}: " + " ".join(f"{k}={v:.3g}" for k, v in m.items()), flush=True)
     assert m["o_gate"] <= TOL_O and m["lse"] <= TOL_LSE, (label, m)
     if grads:
+        alt = None
         for g in ("dq", "dk", "dv"):
-            assert m[g] <= TOL_GRAD, (label, g, m)
+            if m[g] <= TOL_GRAD or g == "dv" or inputs is None:
+                assert m[g] <= TOL_GRAD, (label, g, m)
+                continue
+            if alt is None:
+                alt = ORACLE.backward(*inputs, o_stored=got["o"])
+            shift = float(np.linalg.norm(alt[g] - ref[g]) / np.linalg.norm(ref[g]))
+            r2 = float(np.linalg.norm(got[g] - alt[g]) / np.linalg.norm(alt[g]))
+            print(f"{label}: {g} against D from the stored O: {r2:.3g} (the stored O moves the "
+                  f"reference by {shift:.3g})", flush=True)
+            assert shift > TOL_GRAD / 2 and r2 <= TOL_GRAD, (label, g, m, shift, r2)
         assert m["delta"] <= TOL_DELTA, (label, m)
 
 

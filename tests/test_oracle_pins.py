@@ -394,6 +394,26 @@ def test_forward_rows_matches_full():
         assert np.array_equal(o[rows], orow) and np.array_equal(lse[rows], lrow)
 
 
+def test_backward_with_stored_o_d():
+    """D from a stored O (the page's preprocess definition) against the Jacobian form: with
+    the exact O the identity sum_k P_ik dP_ik = dO_i . O_i makes the two agree; with O
+    perturbed, the gradients move by exactly the induced dS = -P diag(dD) (a closed form)."""
+    rng = np.random.Generator(np.random.PCG64(611))
+    for nq, nk, causal in ((7, 7, True), (5, 9, False), (9, 3, True)):
+        q, k, v, do = (rng.standard_normal((n, 6)) for n in (nq, nk, nk, nq))
+        ref = A.backward(q, k, v, do, 0.4, causal)
+        same = A.backward(q, k, v, do, 0.4, causal, o_stored=ref["o"])
+        for g in ("dq", "dk", "dv"):
+            assert np.allclose(same[g], ref[g], rtol=0, atol=1e-12)
+        eps = 1e-3 * rng.standard_normal(ref["o"].shape)
+        moved = A.backward(q, k, v, do, 0.4, causal, o_stored=ref["o"] + eps)
+        _, _, p = A.forward(q, k, v, 0.4, causal, return_p=True)
+        dd = (do * eps).sum(axis=1, keepdims=True)
+        assert np.allclose(moved["dq"] - ref["dq"], -0.4 * (p * dd) @ k, rtol=0, atol=1e-12)
+        assert np.allclose(moved["dk"] - ref["dk"], -0.4 * (p * dd).T @ q, rtol=0, atol=1e-12)
+        assert np.array_equal(moved["dv"], ref["dv"])
+
+
 def test_dq_rows_matches_full():
     # rows of the full backward's dQ, with fewer queries than keys and rows that see no key
     for nq, nk in ((33, 33), (20, 45), (45, 20)):
