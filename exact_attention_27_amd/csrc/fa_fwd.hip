@@ -66,6 +66,16 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
   constexpr int KB = BN / 32;  // 32-key blocks per tile
   constexpr int NE = 16 * KB;  // scores of a tile per lane
   static_assert(KB == 2, "the instruction interleaving below is laid out for 64-key tiles");
+  // fp16 at d <= 64: the row sum l comes from the matrix cores, in place of 32 VALU adds per
+  // step (at this head dim the VALU, not the matrix cores, bounds the step). Each 16-key group
+  // of P, already packed as the B operand of the P V product, is also the B operand of one
+  // 16x16x32 product whose A operand selects, for each output row, the lanes that hold one
+  // query's keys: with B read in that instruction's layout (lane l: column l%16, k = 8(l/16)+j),
+  // A[m][k] = 1 iff (m/4) and (k/8) have the same parity, and lane l's first result register
+  // (row 4(l/16)) is the sum of its own query's 16 keys. The sum is over P rounded to fp16
+  // (relative error at most 2^-11 in l), so O = sum p v / sum p is normalised by exactly the
+  // weights its product used.
+  constexpr bool MSUM = std::is_same<T, FP16>::value && D == 64 && NW == 4;
 
   // One array per ring slot, every slot index a compile-time constant: the compiler can then
   // tell a copy into one slot from a read of another and does not wait for the copy first.
@@ -181,6 +191,17 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
   // keys of each 32-key block; the two halves are merged in the epilogue).
   float m_run = -INFINITY, m_ref = 0.f, l_run = 0.f;
   float alpha = 1.f;   // rescale factor owed by acc and l before the pending P is added
+  // MSUM: the row sum accumulates in lsum[0] instead (the other registers hold copies)
+  f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f};
+  Frag sel;  // this lane's A elements: A[l%16][8(l/16) + j], all 1 (fp16) or all 0
+  {
+    const uint32_t one2 = (((lane >> 2) ^ (lane >> 4)) & 1) ? 0u : 0x3C003C00u;
+    sel.v = u32x4{one2, one2, one2, one2};
+  }
+  auto rowsum_mfma = [&](const Frag& p) __attribute__((always_inline)) {
+    lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sel.v), __builtin_bit_cast(f16x8, p.v),
+                                                  lsum, 0, 0, 0);
+  };
   bool moved = false;  // this lane's reference moved for the pending tile
 
   // Loop-invariant per-lane byte offsets of every fragment read. The swizzle is linear over
@@ -267,9 +288,9 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c_log2, -m_ref));
         s[kb][i] = e;
-        rs += e;
+        if (!MSUM) rs += e;
       }
-    l_run = __builtin_fmaf(l_run, alpha, rs);
+    if (!MSUM) l_run = __builtin_fmaf(l_run, alpha, rs);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       pf[kb][0] = pack_group<T>(s[kb], 0);
@@ -284,13 +305,16 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      if (MSUM) lsum[0] *= alpha;
     }
   };
   auto pv = [&](const uint16_t* vtile, const Frag (&pf)[KB][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < KB * 2; ++g)
+    for (int g = 0; g < KB * 2; ++g) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] = T::mfma(vfrag(vtile, db, g), pf[g / 2][g % 2], acc[db]);
+      if (MSUM) rowsum_mfma(pf[g / 2][g % 2]);
+    }
   };
 
   // ---- prologue: K(0), V(0), K(1) landed; S(0) and its reference.
@@ -383,6 +407,7 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
         __builtin_amdgcn_sched_barrier(0);
         const int g = j / DB, db = j % DB;
         acc[db] = T::mfma(vf[j % 3], pf[g], acc[db]);
+        if (MSUM && db == DB - 1) rowsum_mfma(pf[g]);
         if (g + 1 < NG) {
           // the next group's 4 packed pairs, PPC of them per chunk (the first 4 chunks of the
           // group when it has more than 4)
@@ -397,7 +422,7 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
 #pragma unroll
         for (int e = 0; e < 32 / NB; ++e) {
           const int idx = j * (32 / NB) + e;
-          rs += s[idx / 16][idx % 16];
+          if (!MSUM) rs += s[idx / 16][idx % 16];
           float x = sn[idx / 16][idx % 16];
           if (MASK) {
             x = masked(x, idx / 16, idx % 16, thr);
@@ -408,7 +433,7 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
         asm volatile("" : "+v"(mx), "+v"(rs));  // keep both running reductions in this chunk
         __builtin_amdgcn_sched_barrier(0);
       }
-      l_run = __builtin_fmaf(l_run, alpha, rs);
+      if (!MSUM) l_run = __builtin_fmaf(l_run, alpha, rs);
       update_ref(mx);
     }
 
@@ -614,7 +639,7 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
   }
 
   // ---- epilogue: one division per row, store O and LSE
-  const float l_tot = half_swap_sum(l_run);
+  const float l_tot = MSUM ? lsum[0] : half_swap_sum(l_run);
   if (SPLIT) {
     if (qrow < N) {
       const size_t r = (size_t)sp * rows_all + sq_.stat + qrow;
