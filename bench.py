@@ -39,6 +39,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -71,11 +72,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """A kernel source without its comments and with every whitespace run collapsed, so that
+    a change of comments alone leaves the hash below, and with it the counter table's claim
+    on the kernel, as it is (the sources hold no "//" inside string literals and no block
+    comments)."""
+    return " ".join(re.sub(r"//[^\n]*", " ", src).split())
+
+
 def source_sha(kernel: str) -> str:
+    """Hash of the code (comments left out) of the sources a kernel is built from."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "exact_attention_27_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_27_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

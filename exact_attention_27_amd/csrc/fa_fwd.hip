@@ -191,7 +191,8 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
   // keys of each 32-key block; the two halves are merged in the epilogue).
   float m_run = -INFINITY, m_ref = 0.f, l_run = 0.f;
   float alpha = 1.f;   // rescale factor owed by acc and l before the pending P is added
-  // MSUM: the row sum accumulates in lsum[0] instead (the other registers hold copies)
+  // MSUM: the row sum accumulates in lsum[0] instead (the product writes the same sum to all
+  // four registers; only lsum[0] is rescaled and read)
   f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f};
   Frag sel;  // this lane's A elements: A[l%16][8(l/16) + j], all 1 (fp16) or all 0
   {

@@ -101,3 +101,13 @@ def test_ingest_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
     assert rec["clock_ghz"] == pytest.approx(1.5)
     assert table["_calibration"]["fetch_factor"] == pytest.approx(4.0)
+
+
+def test_source_hash_ignores_comments_only():
+    """The counter table is tied to a kernel's code: comments and layout may change, code may
+    not. A changed comment or blank line keeps the text that is hashed; a changed token does not."""
+    src = "int f(int x) {  // a comment\n  return x + 1;  // another\n}\n"
+    assert bench.code_text(src) == bench.code_text("int f(int x) {\n\n  // reworded\n  return x + 1;\n}\n")
+    assert bench.code_text(src) != bench.code_text(src.replace("x + 1", "x + 2"))
+    assert "comment" not in bench.code_text(src)
+    assert len(bench.source_sha("fwd")) == 16
