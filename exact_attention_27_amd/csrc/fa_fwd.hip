@@ -28,7 +28,9 @@
 // so the exponentials of one tile run while the matrix cores compute the next tile's scores,
 // and the max reduction runs under the P V products. The ring staggers K one tile ahead of
 // V: step t reads K(t+1) and V(t) while the copies of K(t+2) and V(t+1) land in the slots
-// that held K(t) and V(t-1); one barrier per step publishes them.
+// that held K(t) and V(t-1); one barrier per step publishes them. At d <= 64 (a short step)
+// the ring has three slots each and the copies one step more to land: step t copies K(t+3)
+// and V(t+2), and its barrier waits only for the previous step's copies.
 //
 // Two-group ping-pong (NW = 8, 128-wide tiles, a separate entry point): the matrix product of
 // one query sub-tile runs while the softmax of another runs ("FlashAttention·FA4·FP4", section
@@ -56,7 +58,7 @@ constexpr float kTau = 8.0f;
 // [splits][BH*N][D] accumulators, then [splits][BH*N] maxima, then [splits][BH*N] sums;
 // merge_kernel combines them.
 template <typename T, int D, int BN, int NW, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_kernel(
+__global__ __launch_bounds__(NW * 64, (D <= 64 && NW == 4 && (SPLIT || !CAUSAL)) ? 3 : (D <= 128 && NW == 4) ? 2 : 1) void fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, Geom geo, Strides sq, Strides sk, Strides sv, Strides so,
     int n_qtiles_max, int pair, float c_log2, float* __restrict__ part, long long rows_all, int splits) {
@@ -79,10 +81,15 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
 
   // One array per ring slot, every slot index a compile-time constant: the compiler can then
   // tell a copy into one slot from a read of another and does not wait for the copy first.
+  // RING slots each for K and V: two, or three at d <= 64, where a step is short against the
+  // latency of its tile copies and three workgroups still fit a CU's LDS (48 KB each).
+  constexpr int RING = (D <= 64 && NW == 4) ? 3 : 2;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[RING == 3 ? BN * D : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[RING == 3 ? BN * D : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -168,9 +175,29 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
 
   auto stage_k = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Kh, t * BN, NK, rsk, dh, wave); };
   auto stage_v = [&](int t, uint16_t* dst) { stage_rows_swz_buf<D, BN, NW>(dst, Vh, t * BN, NK, rsv, dh, wave); };
+  // Ring slot I of K / V (a compile-time index).
+  auto kslot = [&](auto ic) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int I = decltype(ic)::value;
+    if constexpr (I == 0) return lds_k0;
+    else if constexpr (I == 1) return lds_k1;
+    else return lds_k2;
+  };
+  auto vslot = [&](auto ic) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int I = decltype(ic)::value;
+    if constexpr (I == 0) return lds_v0;
+    else if constexpr (I == 1) return lds_v1;
+    else return lds_v2;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
   stage_k(t0, lds_k0);
   stage_v(t0, lds_v0);
   stage_k(min(t0 + 1, last), lds_k1);
+  if constexpr (RING == 3) {
+    stage_k(min(t0 + 2, last), kslot(S2()));
+    stage_v(min(t0 + 1, last), lds_v1);
+  }
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qrow][16ks + 8h .. +7].
   Frag qf[KS];
@@ -328,21 +355,21 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
   // Every wave is done with slot k0 before the first step copies K(2) over it.
   ring_barrier();
 
-  // ---- steps t = t0 .. last-1, slot parity P = (t - t0) & 1 fixed at compile time.
+  // ---- steps t = t0 .. last-1, slot phase P = (t - t0) % RING fixed at compile time.
   // (always_inline throughout: at the 256-wide tile these bodies exceed the inliner's budget,
   // and a call would leave the accumulators in scratch memory)
   auto step = [&](auto mask_tag, auto parity_tag, int t) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int P = decltype(parity_tag)::value;
-    const uint16_t* kcur = P ? lds_k0 : lds_k1;  // K(t+1)
-    const uint16_t* vcur = P ? lds_v1 : lds_v0;  // V(t)
-    uint16_t* kdst = P ? lds_k1 : lds_k0;        // K(t+2) replaces K(t)
-    uint16_t* vdst = P ? lds_v0 : lds_v1;        // V(t+1) replaces V(t-1)
-    // Copies of K(t+2) and V(t+1): descriptors now, the copies themselves spread over the
-    // chunks of [A] (issued all at once, the workgroup's waves queue behind each other in the
-    // texture unit right after the barrier).
-    const TileSrc rk = tile_src<D, BN>(Kh, min(t + 2, last) * BN, NK, rsk, dh);
-    const TileSrc rv = tile_src<D, BN>(Vh, (t + 1) * BN, NK, rsv, dh);
+    const uint16_t* kcur = kslot(std::integral_constant<int, (P + 1) % RING>());  // K(t+1)
+    const uint16_t* vcur = vslot(std::integral_constant<int, P>());               // V(t)
+    uint16_t* kdst = kslot(std::integral_constant<int, P>());  // K(t+RING) replaces K(t)
+    uint16_t* vdst = vslot(std::integral_constant<int, (P + RING - 1) % RING>());  // V(t+RING-1) replaces V(t-1)
+    // Copies of K(t+RING) and V(t+RING-1): descriptors now, the copies themselves spread over
+    // the chunks of [A] (issued all at once, the workgroup's waves queue behind each other in
+    // the texture unit right after the barrier).
+    const TileSrc rk = tile_src<D, BN>(Kh, min(t + RING, last) * BN, NK, rsk, dh);
+    const TileSrc rv = tile_src<D, BN>(Vh, (RING == 2 ? t + 1 : min(t + 2, last)) * BN, NK, rsv, dh);
     constexpr int CPW = BN * D * 2 / 1024 / NW;  // copies per wave per tile
 
     // [A] S(t+1) on the matrix cores while the VALU exponentiates S(t). Written out as 16
@@ -438,8 +465,13 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
       update_ref(mx);
     }
 
-    // K(t+2) and V(t+1) must have landed before anyone reads them.
-    wait_async();
+    // K(t+2) and V(t+1) must have landed before anyone reads them: with two slots they are
+    // this step's copies; with three, the previous step's, and this step's may stay in flight
+    // (the counter drains in issue order).
+    if constexpr (RING == 2)
+      wait_async();
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * CPW));  // vmcnt(2 CPW)
     ring_barrier();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
@@ -623,7 +655,7 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
       drain(Even());
     wait_async();
     ring_barrier();
-  } else {
+  } else if constexpr (RING == 2) {
   int t = t0;
   for (; t + 1 < plain_steps; t += 2) {
     step(F(), Even(), t);
@@ -637,6 +669,28 @@ __global__ __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1) void fwd_ke
     drain(Odd());
   else
     drain(Even());
+  } else {
+  int t = t0;
+  for (; t + 2 < plain_steps; t += 3) {
+    step(F(), S0(), t);
+    step(F(), S1(), t + 1);
+    step(F(), S2(), t + 2);
+  }
+  for (; t < last; t += 3) {
+    step(Tr(), S0(), t);
+    if (t + 1 < last) step(Tr(), S1(), t + 1);
+    if (t + 2 < last) step(Tr(), S2(), t + 2);
+  }
+  // The last step's copies (clamped repeats of the last tiles, into free slots) land before
+  // the workgroup moves on; V(last) itself landed before the last step's barrier. Its slot is
+  // picked at run time: one drain body instead of three.
+  wait_async();
+  const int ph = (last - t0) % 3;
+  const uint16_t* vlast = ph == 0 ? lds_v0 : (ph == 1 ? lds_v1 : lds_v2);
+  Frag pf[KB][2];
+  softmax_p(s, pf);
+  rescale();
+  pv(vlast, pf);
   }
 
   // ---- epilogue: one division per row, store O and LSE
