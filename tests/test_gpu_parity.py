@@ -193,6 +193,32 @@ def test_full_size_every_head(fa, key):
     assert dk_sum <= 1e-2 and dv_gap / dv_scale <= 1e-2
 
 
+
+ROWSUM_CASES = [((1, 4, 300, 64), True), ((1, 4, 1000, 64), False), ((2, 2, 777, 32), True), ((1, 2, 129, 40), False)]
+
+
+@pytest.mark.parametrize("shape,causal", ROWSUM_CASES, ids=[f"{'x'.join(map(str, s))}-{'c' if c else 'f'}" for s, c in ROWSUM_CASES])
+def test_fp16_rowsum_lse_bound(fa, shape, causal):
+    """fp16 at d <= 64 sums each row's P after rounding it to fp16, on the matrix cores. Every p
+    then carries a relative rounding error of at most 2^-11, so the row sum and with it exp(LSE)
+    do too: |dLSE| <= 2^-11 (about 4.9e-4), half the general LSE gate. On top of that: p below
+    fp16's normal range is off by at most 2^-25 absolute against a row sum of at least 1 (the
+    reference max never exceeds the row max), and fp32 summation and logarithm error.
+    Checked on every row (the causal first rows hold one, two, three keys)."""
+    B, H, N, d = shape
+    seed = 9600 + ROWSUM_CASES.index((shape, causal))
+    bits = FI.draw_bits(shape, FI.FP16, seed)
+    scale = d ** -0.5
+    gpu = run_gpu(fa, bits, FI.FP16, causal, scale)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            q, k, v = (FI.bits_to_f64(bits[n][b, h], FI.FP16) for n in ("q", "k", "v"))
+            _, lse_ref = ORACLE.forward_rows(q, k, v, scale, causal, np.arange(N))
+            worst = max(worst, float(np.abs(gpu["lse"][b, h] - lse_ref).max()))
+    print(f"fp16 {shape} causal={causal}: max |dLSE| = {worst:.3g}", flush=True)
+    assert worst <= 2.0 ** -11 + N * 2.0 ** -25 + 1e-5, worst
+
 # --------------------------------------------------------------------------- behaviour
 
 def test_forward_without_lse_matches(fa):
