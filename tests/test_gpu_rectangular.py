@@ -11,7 +11,8 @@ against the fp64 oracle on every head, to the tolerances of tests/test_gpu_parit
     ragged key caches (packed sequences of 1-3 queries, one cache empty);
   * packed variable-length batches whose key offsets differ from the query offsets,
     including a sequence with no queries and one with no keys;
-  * the autograd wrapper on K and V sliced out of a packed (B, N_k, 2, H, d) tensor.
+  * the autograd wrapper on K and V sliced out of a packed (B, N_k, 2, H, d) tensor;
+  * the d <= 64 forward's three-slot K/V ring: 1 to 7 key tiles, single-pass and split.
 """
 import numpy as np
 import pytest
@@ -188,6 +189,42 @@ def test_splitkv_rectangular(fa, case):
             compare_head({"o": o_np[b, h], "lse": lse_np[b, h]}, {"o": o_ref, "lse": lse_ref}, dtype,
                          f"split={splits} Nq={Nq} Nk={Nk} d={d} causal={causal} b{b}h{h}", grads=False)
 
+
+
+RING_NK = [1, 63, 64, 65, 128, 129, 191, 192, 193, 256, 257, 320, 385]
+RING_CASES = [(dt, d, c) for dt in (FI.FP16, FI.BF16) for d in (64, 40) for c in (False, True)]
+
+
+@pytest.mark.parametrize("dtype,d,causal", RING_CASES, ids=[f"{dt}-d{d}-{'c' if c else 'f'}" for dt, d, c in RING_CASES])
+def test_forward_ring_residues(fa, dtype, d, causal):
+    """The forward at d <= 64 rotates three K and V slots, so the slot of the last key tile
+    depends on the tile count modulo 3. 1 to 7 key tiles (N_k from 1 to 385, 100 queries),
+    single-pass and split into 2 and 3 key ranges (ranges start at other tiles and hold 0-3
+    tiles), against the oracle on every head."""
+    import torch
+    B, H, Nq = 1, 2, 100
+    scale = d ** -0.5
+    for nk in RING_NK:
+        bits = FI.draw_bits_rect(B, H, Nq, nk, d, dtype, 6700 + nk + d)
+        q, k, v = (_lib.to_device(bits[n], dtype) for n in ("q", "k", "v"))
+        refs = {}
+        for h in range(H):
+            qf, kf, vf = (FI.bits_to_f64(bits[n][0, h], dtype) for n in ("q", "k", "v"))
+            refs[h] = ORACLE.forward(qf, kf, vf, scale, causal)
+        for splits in (0, 2, 3):
+            o, lse = _nan_like(q), _nan_like(q, (B, H, Nq))
+            if splits:
+                need = fa.fa_forward_splitkv_ex_workspace_bytes(q, k, splits, layout="bhnd")
+                ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=q.device)
+                fa.fa_forward_splitkv_ex(q, k, v, o, lse, causal, scale, splits, ws, layout="bhnd")
+            else:
+                fa.fa_forward_ex(q, k, v, o, lse, causal, scale, layout="bhnd")
+            torch.cuda.synchronize()
+            o_np, lse_np = _lib.from_device(o, dtype), lse.cpu().numpy().astype(np.float64)
+            for h in range(H):
+                o_ref, lse_ref = refs[h]
+                compare_head({"o": o_np[0, h], "lse": lse_np[0, h]}, {"o": o_ref, "lse": lse_ref}, dtype,
+                             f"Nk={nk} splits={splits} h{h}", grads=False)
 
 # ------------------------------------------------------ variable lengths, separate key offsets
 
