@@ -41,6 +41,12 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
   constexpr int DB = D / 32;
   constexpr int CPW = BQ * D * 2 / 1024 / NW;  // tile copies per wave per Q (or dO) tile
   static_assert(CPW >= 1, "each wave copies at least one KB of a tile");
+  // d <= 64: D folded into the dP product. The wave's V rows are negated once in LDS and each
+  // step's dP accumulator starts from D, so the product gives D - dP and P (D - dP) = -dS costs
+  // one multiply per element instead of a subtract and a multiply; dK then accumulates -dK and
+  // is scaled by -scale. (At d = 128 the 16 registers the initial value needs at the start of
+  // the dP phase push spills into the loop.)
+  constexpr bool DFOLD = D <= 64;
 
   // The workgroup's V tile stays in LDS; Q/dO tiles stream. All tiles are swizzled (row and
   // transposed reads are both conflict-free). One array per ring slot, every slot index a
@@ -150,6 +156,16 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     }
   wait_async();
   __syncthreads();
+  if constexpr (DFOLD) {
+    // this wave's V rows, the only ones it reads, sign-flipped in place (exact)
+    u32x4* vw = reinterpret_cast<u32x4*>(lds_v + wave * 32 * D);
+#pragma unroll
+    for (int c = 0; c < 32 * D * 2 / 16 / 64; ++c) {
+      u32x4 x = vw[c * 64 + lane];
+      x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      vw[c * 64 + lane] = x;
+    }
+  }
 
   // Loop-invariant per-lane byte offsets of every fragment read (the swizzle is linear over
   // XOR): row reads of Q / dO / V need one offset per k-step, transposing reads of Q / dO two
@@ -230,6 +246,15 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
     {
       constexpr int EPC = 16 / KS;  // elements per chunk
       Frag dfr[2], vfr[2];
+      f32x16 dini;  // DFOLD: D of register i's row, the dP accumulator's initial value
+      if constexpr (DFOLD) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d4 = st_read(kStatB, g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dini[4 * g + e] = d4[e];
+        }
+      }
       dfr[0] = lds_read_rows(dos, rofs[0]);
       vfr[0] = lds_read_rows(lds_v, rofs[0] + vrow);
 #pragma unroll
@@ -239,9 +264,9 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
           vfr[(ks + 1) % 2] = lds_read_rows(lds_v, rofs[ks + 1] + vrow);
         }
         if ((ks * EPC) % 4 == 0 && (ks * EPC) / 4 + 1 < 4) st4[(ks * EPC) / 4 + 1] = st_read(0, (ks * EPC) / 4 + 1);
-        if (ks == KS - 1) st4[0] = st_read(kStatB, 0);
+        if (!DFOLD && ks == KS - 1) st4[0] = st_read(kStatB, 0);
         __builtin_amdgcn_sched_barrier(0);
-        dp = T::mfma(dfr[ks % 2], vfr[ks % 2], ks == 0 ? f32x16{} : dp);
+        dp = T::mfma(dfr[ks % 2], vfr[ks % 2], ks == 0 ? (DFOLD ? dini : f32x16{}) : dp);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
           const int i = ks * EPC + e;
@@ -268,13 +293,14 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         if (j + 1 < NJ) tfr[(j + 1) % 2] = tfrag(dos, (j + 1) % DB, ((j + 1) / DB) * 16);
-        if ((j * EPC) % 4 == 0 && (j * EPC) / 4 + 1 < 4) st4[(j * EPC) / 4 + 1] = st_read(kStatB, (j * EPC) / 4 + 1);
+        if (!DFOLD && (j * EPC) % 4 == 0 && (j * EPC) / 4 + 1 < 4)
+          st4[(j * EPC) / 4 + 1] = st_read(kStatB, (j * EPC) / 4 + 1);
         __builtin_amdgcn_sched_barrier(0);
         acc_dv[j % DB] = T::mfma(tfr[j % 2], pf[j / DB], acc_dv[j % DB]);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
           const int i = j * EPC + e;
-          dp[i] = s[i] * (dp[i] - st4[i / 4][i % 4]);
+          dp[i] = DFOLD ? s[i] * dp[i] : s[i] * (dp[i] - st4[i / 4][i % 4]);  // DFOLD: -dS
           if (i % 2 == 1) df[i / 8].v[(i % 8) / 2] = T::pack2(dp[i - 1], dp[i]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -330,8 +356,9 @@ __global__ __launch_bounds__(NW * 64, D <= 128 ? 2 : 1) void bwd_dkv_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 wk, wv;
-        wk[0] = T::pack2(acc_dk[db][4 * g + 0] * scale, acc_dk[db][4 * g + 1] * scale);
-        wk[1] = T::pack2(acc_dk[db][4 * g + 2] * scale, acc_dk[db][4 * g + 3] * scale);
+        constexpr float sgn = DFOLD ? -1.f : 1.f;  // DFOLD: acc_dk holds -dK / scale
+        wk[0] = T::pack2(acc_dk[db][4 * g + 0] * (sgn * scale), acc_dk[db][4 * g + 1] * (sgn * scale));
+        wk[1] = T::pack2(acc_dk[db][4 * g + 2] * (sgn * scale), acc_dk[db][4 * g + 3] * (sgn * scale));
         wv[0] = T::pack2(acc_dv[db][4 * g + 0], acc_dv[db][4 * g + 1]);
         wv[1] = T::pack2(acc_dv[db][4 * g + 2], acc_dv[db][4 * g + 3]);
         // columns db*32 + 8g + 4h .. +3 exist iff db*32 + 8g < dh (dh is a multiple of 8): a
