@@ -599,7 +599,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the path shards over batch*heads with no communication, but no multi-GPU run is provided.",
               file=sys.stderr)
         sys.exit(2)

@@ -54,7 +54,7 @@
  *              FA_ERR_INVALID_ARG for null/misaligned/overlapping pointers,
  *              non-positive sizes, 64-bit size overflow, unknown dtype, a causal
  *              flag other than 0/1, or a non-finite / non-positive scale;
- *              FA_ERR_UNSUPPORTED for a valid request this build does not implement
+ *              FA_ERR_UNSUPPORTED for a valid request the library does not implement
  *              (head dim above 256 or not a multiple of 8); FA_ERR_HIP if one of this call's
  *              kernel launches fails (each launch's own status: an error left pending on the
  *              thread by an earlier, unrelated HIP call is not reported as this call's).
