@@ -25,7 +25,10 @@
  *              also take strided operands and variable-length batches.
  *   Types      dtype FA_FP16 (IEEE binary16) or FA_BF16 (bfloat16). Arithmetic is
  *              fp32 inside (fp32 accumulation on the matrix cores); every fp32 ->
- *              16-bit conversion rounds to nearest even.
+ *              16-bit conversion rounds to nearest even. The forward's row sum of P is
+ *              taken over fp32 P, except for fp16 at d <= 64, where it sums (in fp32) the
+ *              P rounded to fp16 that the P V product uses: LSE then moves by at most
+ *              2^-11 (about 4.9e-4) against the fp32 sum.
  *   Shapes     B, H, N >= 1; head dim d a multiple of 8 up to 256 (d <= 64 runs on the
  *              64-wide kernels, d <= 128 on the 128-wide ones, larger d on the 256-wide
  *              ones, with the columns past d zero on chip: exact, at the cost of the
